@@ -1,0 +1,44 @@
+"""fp64 CPU oracle for exact tiled attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this package: only the test suite, the smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code, constants or helpers
+with the HIP library; inputs reach both sides from the seeded generators in
+``exact_tiled_attention_04_amd.workloads``, which hold none of the method's
+arithmetic.
+
+Every function here is the plain definition of what the GPU path computes,
+written out in float64 with numpy and materialising the full score and
+probability matrices, so that a reader can check it against the pages by eye:
+
+* ``forward``       -- S = scale * Q K^T (+ causal mask), P = softmax(S),
+                       O = P V, and the per-row log-sum-exp.
+* ``decode_paged``  -- one query per sequence against a paged KV cache,
+                       gathered through the block table, then ``forward``'s
+                       definition with no mask.
+* ``backward``      -- gradients of sum(O * dO) with P recomputed from the
+                       definition (textbook softmax Jacobian).
+* ``brute_force_forward`` -- scalar pure-Python loops, tiny inputs only; a
+                       second, structurally different evaluation used to pin
+                       ``forward``.
+
+Pins (tests/test_oracle.py): brute force on N <= 8, closed forms (Q = 0,
+one-hot dominant score), softmax invariants, translation invariance of the
+keys, torch's fp64 CPU scaled_dot_product_attention and autograd as
+independent library evaluations, central finite differences for the
+gradients, the Flash-attention (aigrafen.se) worked example's fp32
+deviation, paged-gather equivalences and planted-mistake checks.  Absolute
+O / LSE values of the seeded workloads are printed nowhere on the pages:
+those values are anchored only by the definition and the pins above
+("parity unpinned" by printed values).
+"""
+
+from .attention import (  # noqa: F401
+    backward,
+    brute_force_backward_dv,
+    brute_force_forward,
+    decode_paged,
+    forward,
+    forward_probs,
+    gather_paged,
+)
