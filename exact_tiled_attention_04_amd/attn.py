@@ -1,0 +1,224 @@
+"""Thin ctypes binding over libeta_attn.so (see include/attn.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and torch's current HIP stream are passed
+to the C ABI, and a non-OK status raises.  Every step of the computation runs
+in the library's HIP kernels.  There is no fallback: if the library has not
+been built (``python -m exact_tiled_attention_04_amd.build``) the first call
+raises.
+
+Names follow the C ABI: ``attn_fwd``, ``attn_decode_paged``, ``attn_bwd``,
+``attn_decode_paged_workspace_size``, ``attn_bwd_workspace_size``,
+``attn_plan_describe``, ``attn_status_string``.
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeta_attn.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_WORKSPACE = 3
+ATTN_ERR_HIP = 4
+
+ATTN_DTYPE_F32 = 0
+ATTN_DTYPE_BF16 = 1
+
+ATTN_PHASE_FWD = 0
+ATTN_PHASE_DECODE = 1
+ATTN_PHASE_BWD = 2
+
+EXPORTED = (
+    "attn_fwd",
+    "attn_decode_paged_workspace_size",
+    "attn_decode_paged",
+    "attn_bwd_workspace_size",
+    "attn_bwd",
+    "attn_plan_describe",
+    "attn_status_string",
+    "attn_last_error",
+)
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{_status_name(status)}: {detail}")
+
+
+def load_library(path=LIB_PATH):
+    """Load (once) and return the ctypes handle, with prototypes set."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m exact_tiled_attention_04_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    lib.attn_fwd.restype = i32
+    lib.attn_decode_paged_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.attn_decode_paged_workspace_size.restype = sz
+    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                      i32, i32, i64, i64, i64, f32, i32, i32, vp, sz, vp]
+    lib.attn_decode_paged.restype = i32
+    lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.attn_bwd_workspace_size.restype = sz
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                             f32, i32, i32, vp, sz, vp]
+    lib.attn_bwd.restype = i32
+    lib.attn_plan_describe.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                       ctypes.c_char_p, sz]
+    lib.attn_plan_describe.restype = i32
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_name(status):
+    try:
+        return load_library().attn_status_string(status).decode()
+    except Exception:  # pragma: no cover - only when the library is absent
+        return f"status {status}"
+
+
+def _check(status):
+    if status != ATTN_OK:
+        raise AttnError(status, load_library().attn_last_error().decode())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return ATTN_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need_device(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def attn_fwd(q, k, v, scale, causal, out=None, lse=None, stream=None):
+    """O, LSE = attention(q, k, v).  q [B,H,Nq,d]; k, v [B,Hkv,Nk,d]."""
+    lib = load_library()
+    _need_device(q, k, v)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, Nk, d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _need_device(out, lse)
+    _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Nq, Nk, d,
+                        float(scale), int(bool(causal)), _dtype_code(q), _stream(stream)))
+    return out, lse
+
+
+def attn_decode_paged_workspace_size(num_seqs, Hq, d, max_context, chunk_tokens=0):
+    return int(load_library().attn_decode_paged_workspace_size(num_seqs, Hq, d, max_context,
+                                                               chunk_tokens))
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, scale, max_context,
+                      chunk_tokens=0, strides=None, out=None, lse=None, workspace=None,
+                      stream=None):
+    """Paged GQA decode.
+
+    q [num_seqs, Hq, d]; k_cache, v_cache [num_blocks, block_size, Hkv, d]
+    (or any layout described by ``strides`` = (block, token, head) in
+    elements, with ``k_cache`` shaped so that dim 0 counts blocks, dim 1 the
+    slots and dim 2 the KV heads); block_table int32 [num_seqs, max_blocks];
+    context_lens int32 [num_seqs] on the device.
+    """
+    lib = load_library()
+    _need_device(q, k_cache, v_cache, block_table, context_lens)
+    num_seqs, Hq, d = q.shape
+    num_blocks, block_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_table and context_lens must be int32")
+    max_blocks = block_table.shape[1]
+    if strides is None:
+        strides = (block_size * Hkv * d, Hkv * d, d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((num_seqs, Hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_paged_workspace_size(num_seqs, Hq, d, max_context, chunk_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_decode_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(context_lens),
+        _ptr(out), _ptr(lse), num_seqs, Hq, Hkv, d, block_size, num_blocks, max_blocks,
+        int(max_context), int(strides[0]), int(strides[1]), int(strides[2]), float(scale),
+        _dtype_code(q), int(chunk_tokens), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def attn_bwd_workspace_size(B, H, Nq, d):
+    return int(load_library().attn_bwd_workspace_size(B, H, Nq, d))
+
+
+def attn_bwd(q, k, v, o, do, lse, scale, causal, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
+    """dQ, dK, dV of attention given the forward's O and LSE."""
+    lib = load_library()
+    _need_device(q, k, v, o, do, lse)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_size(B, H, Nq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                        _ptr(dk), _ptr(dv), B, H, Hkv, Nq, Nk, d, float(scale),
+                        int(bool(causal)), _dtype_code(q), _ptr(workspace), workspace.numel(),
+                        _stream(stream)))
+    return dq, dk, dv
+
+
+def attn_plan_describe(phase, B, H, Hkv, Nq, Nk, d, causal, dtype=ATTN_DTYPE_BF16):
+    lib = load_library()
+    buf = ctypes.create_string_buffer(512)
+    n = lib.attn_plan_describe(phase, B, H, Hkv, Nq, Nk, d, int(bool(causal)), dtype, buf, 512)
+    if n < 0:
+        raise ValueError("invalid arguments for attn_plan_describe")
+    return buf.value.decode()
+
+
+def attn_status_string(status):
+    return load_library().attn_status_string(status).decode()

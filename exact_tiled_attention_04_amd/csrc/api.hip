@@ -1,0 +1,287 @@
+// C-ABI entry points: argument validation, planning and launches.
+//
+// Validation happens entirely on the host before anything is enqueued, so a
+// rejected call touches neither the device nor the stream.  The planner is a
+// pure function of the shapes ("Modern attention kernels", "Work
+// partitioning in FlashAttention-2": kernel selection needs batch, heads,
+// sequence length and head dimension; "Prefill and decode need different
+// kernels": record the choice per phase).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+attn_status_t ok() {
+  g_last_error[0] = '\0';
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int kNumCU = 256;        // MI355X compute units
+constexpr long long kMaxGrid = 0x7fffffffLL;
+
+// ---------------------------------------------------------------- forward
+
+eta::FwdPlan plan_fwd(int B, int H, int Nq, bool bf16) {
+  eta::FwdPlan p;
+  if (bf16) {
+    // One wave = 32 query rows.  Four waves per workgroup share each K/V
+    // tile; when that leaves fewer than two workgroups per CU, halve the
+    // workgroup so the causal work spreads over more CUs.
+    p.waves = 4;
+    long long wgs = (long long)B * H * ((Nq + 127) / 128);
+    if (wgs < 2LL * kNumCU) p.waves = 2;
+    p.block_keys = 64;
+  } else {
+    p.waves = 4;
+    p.block_keys = 32;
+  }
+  p.block_rows = 32 * p.waves;
+  p.workgroups = (long long)B * H * ((Nq + p.block_rows - 1) / p.block_rows);
+  return p;
+}
+
+attn_status_t check_fwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                              attn_dtype_t dtype) {
+  if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d H=%d Hkv=%d Nq=%d Nk=%d)", B, H,
+                Hkv, Nq, Nk);
+  if (H % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+  if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16)
+    return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(ATTN_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension %d not in {64,128}", d);
+  const long long rows = (long long)B * H * Nq;
+  if (rows * d > (1LL << 46)) return fail(ATTN_ERR_INVALID_ARG, "tensor too large");
+  return ATTN_OK;
+}
+
+// ----------------------------------------------------------------- decode
+
+int plan_decode_chunk(int num_seqs, int Hkv, int max_context, int chunk_tokens) {
+  if (chunk_tokens > 0) return chunk_tokens;
+  // Aim for about 32 waves per CU over the whole launch when every sequence
+  // is as long as max_context: enough independent K/V streams in flight to
+  // cover HBM latency, few enough partials that the merge stays small.
+  const long long target_units = 32LL * kNumCU;
+  const long long pairs = (long long)num_seqs * Hkv;
+  long long chunk = (pairs * (long long)max_context + target_units - 1) / target_units;
+  chunk = (chunk + 31) / 32 * 32;
+  if (chunk < 256) chunk = 256;
+  if (chunk > 8192) chunk = 8192;
+  return (int)chunk;
+}
+
+attn_status_t check_decode_shape(int num_seqs, int Hq, int Hkv, int d, int block_size,
+                                 int num_blocks, int max_blocks_per_seq, int max_context,
+                                 int chunk_tokens) {
+  if (num_seqs < 1 || Hq < 1 || Hkv < 1 || block_size < 1 || num_blocks < 1 ||
+      max_blocks_per_seq < 1 || max_context < 0)
+    return fail(ATTN_ERR_INVALID_ARG,
+                "bad decode sizes (num_seqs=%d Hq=%d Hkv=%d block_size=%d num_blocks=%d "
+                "max_blocks_per_seq=%d max_context=%d)",
+                num_seqs, Hq, Hkv, block_size, num_blocks, max_blocks_per_seq, max_context);
+  if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension %d not in {64,128}", d);
+  if ((long long)max_context > (long long)max_blocks_per_seq * block_size)
+    return fail(ATTN_ERR_INVALID_ARG, "max_context=%d exceeds block table capacity %lld",
+                max_context, (long long)max_blocks_per_seq * block_size);
+  if (chunk_tokens < 0 || chunk_tokens % 32 != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "chunk_tokens=%d must be 0 or a positive multiple of 32",
+                chunk_tokens);
+  return ATTN_OK;
+}
+
+// --------------------------------------------------------------- backward
+
+attn_status_t check_bwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                              attn_dtype_t dtype) {
+  attn_status_t st = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_DTYPE_BF16) return fail(ATTN_ERR_UNSUPPORTED, "backward supports bf16 only");
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                       int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                       attn_dtype_t dtype, void* stream) {
+  if (!Q || !K || !V || !O || !LSE) return fail(ATTN_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return fail(ATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  attn_status_t st = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  eta::FwdArgs a{Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, causal, dtype == ATTN_DTYPE_BF16};
+  eta::FwdPlan p = plan_fwd(B, H, Nq, a.dtype_bf16);
+  if (p.workgroups > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "grid too large");
+  hipError_t e = eta::launch_fwd(a, p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_context,
+                                        int chunk_tokens) {
+  if (num_seqs < 1 || Hq < 1 || (d != 64 && d != 128) || max_context < 0 || chunk_tokens < 0 ||
+      chunk_tokens % 32 != 0)
+    return 0;
+  // The plan only needs Hkv to pick a chunk; the workspace must cover the
+  // largest chunk count any Hkv could lead to, i.e. the smallest chunk.
+  const int chunk = chunk_tokens > 0 ? chunk_tokens : plan_decode_chunk(num_seqs, 1, max_context, 0);
+  const int n_chunks = (max_context + chunk - 1) / chunk;
+  return eta::decode_workspace_bytes(num_seqs, Hq, d, n_chunks > 0 ? n_chunks : 1);
+}
+
+attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache,
+                                const int32_t* block_table, const int32_t* context_lens, void* O,
+                                float* LSE, int num_seqs, int Hq, int Hkv, int d, int block_size,
+                                int num_blocks, int max_blocks_per_seq, int max_context,
+                                int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                                float scale, attn_dtype_t dtype, int chunk_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Q || !K_cache || !V_cache || !block_table || !context_lens || !O)
+    return fail(ATTN_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(Q) || !aligned16(K_cache) || !aligned16(V_cache) || !aligned16(O) ||
+      ((uintptr_t)block_table & 3u) || ((uintptr_t)context_lens & 3u) ||
+      (LSE && ((uintptr_t)LSE & 3u)))
+    return fail(ATTN_ERR_INVALID_ARG, "misaligned pointer argument");
+  attn_status_t st = check_decode_shape(num_seqs, Hq, Hkv, d, block_size, num_blocks,
+                                        max_blocks_per_seq, max_context, chunk_tokens);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_DTYPE_BF16) {
+    if (dtype != ATTN_DTYPE_F32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    return fail(ATTN_ERR_UNSUPPORTED, "paged decode supports bf16 only");
+  }
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(ATTN_ERR_INVALID_ARG, "scale must be positive and finite");
+  // Layout identity ("Failure modes": page-table mismatch): the strides must
+  // describe disjoint, 16-byte aligned rows.
+  if (head_stride < d || token_stride < (int64_t)Hkv * head_stride ||
+      block_stride < (int64_t)block_size * token_stride || head_stride % 8 || token_stride % 8 ||
+      block_stride % 8)
+    return fail(ATTN_ERR_INVALID_ARG,
+                "cache strides inconsistent with block_size=%d Hkv=%d d=%d "
+                "(block=%lld token=%lld head=%lld)",
+                block_size, Hkv, d, (long long)block_stride, (long long)token_stride,
+                (long long)head_stride);
+  const int chunk = plan_decode_chunk(num_seqs, Hkv, max_context, chunk_tokens);
+  const int n_chunks = (max_context + chunk - 1) / chunk;
+  const size_t need = eta::decode_workspace_bytes(num_seqs, Hq, d, n_chunks > 0 ? n_chunks : 1);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  eta::DecodeArgs a{Q,        K_cache,     V_cache,      block_table,  context_lens,
+                    O,        LSE,         num_seqs,     Hq,           Hkv,
+                    d,        block_size,  num_blocks,   max_blocks_per_seq,
+                    max_context, block_stride, token_stride, head_stride, scale,
+                    workspace};
+  eta::DecodePlan p{chunk, n_chunks};
+  hipError_t e = eta::launch_decode(a, p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t attn_bwd_workspace_size(int B, int H, int Nq, int d) {
+  if (B < 1 || H < 1 || Nq < 1 || (d != 64 && d != 128)) return 0;
+  return eta::bwd_workspace_bytes(B, H, Nq, d);
+}
+
+attn_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                       const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv,
+                       int Nq, int Nk, int d, float scale, int causal, attn_dtype_t dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV)
+    return fail(ATTN_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
+    return fail(ATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  attn_status_t st = check_bwd_shape(B, H, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  const size_t need = eta::bwd_workspace_bytes(B, H, Nq, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "backward workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  eta::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Hkv, Nq, Nk, d, scale, causal, workspace};
+  hipError_t e = eta::launch_bwd(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int attn_plan_describe(int phase, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                       attn_dtype_t dtype, char* buf, size_t len) {
+  char tmp[512];
+  int n = -1;
+  if (phase == ATTN_PHASE_FWD) {
+    if (check_fwd_shape(B, H, Hkv, Nq, Nk, d, 1.f, dtype) != ATTN_OK) return -1;
+    const bool bf16 = dtype == ATTN_DTYPE_BF16;
+    eta::FwdPlan p = plan_fwd(B, H, Nq, bf16);
+    n = snprintf(tmp, sizeof(tmp),
+                 "phase=fwd kernel=%s d=%d causal=%d Br=%d (%d waves x 32 rows) Bc=%d "
+                 "grid=%lld workgroups (B*H*ceil(Nq/Br)) order=heavy-query-tiles-first "
+                 "head-interleaved",
+                 bf16 ? "fwd_bf16_mfma32x32x16" : "fwd_f32_mfma32x32x2", d, causal ? 1 : 0,
+                 p.block_rows, p.waves, p.block_keys, p.workgroups);
+  } else if (phase == ATTN_PHASE_DECODE) {
+    if (check_decode_shape(B, H, Hkv, d, 16, 1, (Nk + 15) / 16 > 0 ? (Nk + 15) / 16 : 1, Nk, 0) !=
+        ATTN_OK)
+      return -1;
+    const int chunk = plan_decode_chunk(B, Hkv, Nk, 0);
+    const int n_chunks = (Nk + chunk - 1) / chunk;
+    n = snprintf(tmp, sizeof(tmp),
+                 "phase=decode kernel=decode_split_mfma16x16x32+decode_merge d=%d G=%d "
+                 "chunk_tokens=%d max_chunks=%d split_waves<=%lld (seqs*Hkv*chunks) "
+                 "merge_workgroups=%lld",
+                 d, H / Hkv, chunk, n_chunks, (long long)B * Hkv * n_chunks, (long long)B * H);
+  } else if (phase == ATTN_PHASE_BWD) {
+    if (check_bwd_shape(B, H, Hkv, Nq, Nk, d, 1.f, dtype) != ATTN_OK) return -1;
+    n = snprintf(tmp, sizeof(tmp),
+                 "phase=bwd kernels=bwd_pre+bwd_main_mfma32x32x16+bwd_dq d=%d causal=%d "
+                 "key_tile=128 (4 waves x 32 keys) query_tile=64 grid=%lld workgroups "
+                 "(B*Hkv*ceil(Nk/128)) dq=fp32-atomics",
+                 d, causal ? 1 : 0, (long long)B * Hkv * ((Nk + 127) / 128));
+  } else {
+    return -1;
+  }
+  if (buf && len > 0) {
+    strncpy(buf, tmp, len - 1);
+    buf[len - 1] = '\0';
+  }
+  return n;
+}
+
+const char* attn_status_string(attn_status_t status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+  }
+  return "ATTN_ERR_UNKNOWN";
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Device helpers shared by the attention kernels (gfx950 / CDNA4 only).
+//
+// MFMA operand layouts used throughout (wave64; verified on gfx950):
+//   v_mfma_f32_32x32x16_bf16  C[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[l%32][8*(l/32) + e], e = 0..7
+//     B: lane l holds B[8*(l/32) + e][l%32]
+//     C: lane l, register r holds C[8*(r/4) + 4*(l/32) + r%4][l%32]
+//   v_mfma_f32_16x16x32_bf16  C[16x16] += A[16x32] * B[32x16]
+//     A: lane l holds A[l%16][8*(l/16) + e]
+//     B: lane l holds B[8*(l/16) + e][l%16]
+//     C: lane l, register r holds C[4*(l/16) + r][l%16]
+//   ds_read_b64_tr_b16 (per group of 16 lanes): source lane s supplies the
+//     address of 4 consecutive 16-bit values; they form row s/4, columns
+//     4*(s%4)..4*(s%4)+3 of a 4x16 block, and lane j receives column j
+//     (rows 0..3) of that block.  Pointing the four lanes of row r at
+//     M[k0 + r][n0 .. n0 + 15] therefore hands lane j the values
+//     M[k0 .. k0+3][n0 + j]: a column read of a row-major tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eta {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (inputs below -126 give 0, -inf gives 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round-to-nearest-even pack of two floats into two bf16 (low = a).
+__device__ __forceinline__ unsigned int pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(unsigned int, v);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(unsigned short h) {
+  return __builtin_bit_cast(float, ((unsigned int)h) << 16);
+}
+
+// LDS transpose read of 4 bf16 (see header comment for the lane mapping).
+__device__ __forceinline__ s16x4 lds_read_tr(const void* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)(size_t)lds_ptr));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(const s16x4& lo, const s16x4& hi) {
+  u32x4 r;
+  u32x2 a = __builtin_bit_cast(u32x2, lo);
+  u32x2 b = __builtin_bit_cast(u32x2, hi);
+  r[0] = a[0];
+  r[1] = a[1];
+  r[2] = b[0];
+  r[3] = b[1];
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Value of lane (l ^ 32): the other half of the wave.
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Wave-uniform "any lane true".
+__device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
+
+}  // namespace eta

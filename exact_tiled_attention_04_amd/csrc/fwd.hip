@@ -1,0 +1,459 @@
+// Tiled exact attention forward (prefill) for gfx950.
+//
+// Method ("Modern attention kernels", sections "Online softmax makes tiling
+// exact" and "Kernel structure"; "Attention kernels", online-softmax
+// derivation): each workgroup owns one query tile of one (batch, head); it
+// keeps the queries in registers, streams the key/value tiles its mask allows
+// through LDS, and carries a running maximum m, running sum l and an
+// unnormalised accumulator o per query row.  After the last tile it divides
+// once and writes O and the per-row log-sum-exp; the score and probability
+// tiles never leave the chip.
+//
+// Mapping onto CDNA4:
+//   * one wave = 32 query rows; the score tile is computed transposed,
+//     S^T = K Q^T, on v_mfma_f32_32x32x16_bf16 so that each lane holds the
+//     scores of ONE query row (16 keys per 32-key block); row max and row sum
+//     are in-register plus one exchange between the two half-waves;
+//   * o^T = V^T P^T on the same MFMA, P taken straight from the score
+//     registers (packed to bf16), V^T read from the row-major V tile in LDS
+//     with ds_read_b64_tr_b16;
+//   * the softmax runs in base 2 with scale*log2(e) folded into one FMA;
+//   * K/V tiles are double-buffered in LDS with a register prefetch of the
+//     next tile, one barrier per tile;
+//   * grid = batch x head x query tile ("Work partitioning in
+//     FlashAttention-2": parallel over the sequence), causal tiles heaviest
+//     first, consecutive workgroups on different heads so that each XCD's L2
+//     serves a fixed subset of heads.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace eta {
+
+namespace {
+
+constexpr int kBC = 64;  // keys per K/V tile
+
+// XOR swizzle of 16-byte chunks within an LDS row (removes bank conflicts of
+// the column-of-rows access patterns).  CH = chunks per row.
+template <int CH>
+__device__ __forceinline__ int swz(int row) {
+  return row & (CH - 1);
+}
+
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
+    int B, int H, int Hkv, int Nq, int Nk, float scale_log2, int n_qtiles) {
+  constexpr int NT = NW * 64;
+  constexpr int BR = NW * 32;
+  constexpr int CH = D / 8;                  // 16-byte chunks per row
+  constexpr int NLOAD = kBC * CH / NT;       // 16-byte loads per thread per tile
+  constexpr int KS = D / 16;                 // k-steps of the QK^T product
+  constexpr int NB = D / 32;                 // 32-wide column blocks of o
+  static_assert(kBC * CH % NT == 0, "tile load split");
+
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][kBC * D];  // [buf][K|V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 31;   // query row within the wave / A-row
+  const int hh = lane >> 5;   // half-wave
+
+  const int BH = B * H;
+  const int wg = blockIdx.x;
+  const int qt = n_qtiles - 1 - wg / BH;  // heavy (late) query tiles first
+  const int bh = wg % BH;
+  const int b = bh / H;
+  const int h = bh % H;
+  const int g = h / (H / Hkv);
+  const int q0 = qt * BR;
+  const int off = Nk - Nq;  // bottom-right causal alignment
+
+  const __bf16* Qp = Q + ((size_t)b * H + h) * (size_t)Nq * D;
+  const __bf16* Kp = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+  const __bf16* Vp = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+  __bf16* Op = O + ((size_t)b * H + h) * (size_t)Nq * D;
+  float* Lp = LSE + ((size_t)b * H + h) * (size_t)Nq;
+
+  const int qrow = q0 + wave * 32 + li;
+  const int wave_row_lo = q0 + wave * 32;
+
+  // Number of key tiles this query tile can see.
+  int n_tiles;
+  if (CAUSAL) {
+    int last = min(Nk - 1, q0 + BR - 1 + off);
+    n_tiles = last < 0 ? 0 : last / kBC + 1;
+  } else {
+    n_tiles = (Nk + kBC - 1) / kBC;
+  }
+
+  // Queries of this lane's row as the B operand (Q^T), zero past Nq.
+  bf16x8 qf[KS];
+  {
+    const bool ok = qrow < Nq;
+    const __bf16* src = Qp + (size_t)(ok ? qrow : 0) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = ok ? *(const u32x4*)(src + 16 * ks + 8 * hh) : u32x4{0, 0, 0, 0};
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x16 o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x16{};
+  float m_run = -INFINITY;  // running max, base-2 units (scores * scale * log2 e)
+  float l_run = 0.f;        // this lane's partial running sum
+
+  u32x4 pk[NLOAD], pv[NLOAD];
+  auto load_tile = [&](int t) {
+    const int k0 = t * kBC;
+#pragma unroll
+    for (int it = 0; it < NLOAD; ++it) {
+      const int cid = tid + it * NT;
+      const int row = cid / CH;
+      const int c = cid % CH;
+      const int key = k0 + row;
+      if (key < Nk) {
+        pk[it] = *(const u32x4*)(Kp + (size_t)key * D + c * 8);
+        pv[it] = *(const u32x4*)(Vp + (size_t)key * D + c * 8);
+      } else {
+        pk[it] = u32x4{0, 0, 0, 0};
+        pv[it] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < NLOAD; ++it) {
+      const int cid = tid + it * NT;
+      const int row = cid / CH;
+      const int c = cid % CH;
+      const int idx = row * D + ((c ^ swz<CH>(row)) * 8);
+      *(u32x4*)(&smem[buf][0][idx]) = pk[it];
+      *(u32x4*)(&smem[buf][1][idx]) = pv[it];
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    const int k0 = t * kBC;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+
+    // Tiles wholly above this wave's diagonal contribute nothing.
+    const bool wave_live = !CAUSAL || (k0 <= wave_row_lo + 31 + off);
+    if (wave_live) {
+      const __bf16* Ks = smem[buf][0];
+      const __bf16* Vs = smem[buf][1];
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        const int row = 32 * kb + li;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = *(const bf16x8*)(Ks + row * D + (((2 * ks + hh) ^ swz<CH>(row)) * 8));
+          s[kb] = mfma32(a, qf[ks], s[kb]);
+        }
+      }
+
+      // Mask the causal boundary and the ragged key tail.
+      const bool need_mask = (k0 + kBC > Nk) || (CAUSAL && (k0 + kBC - 1 > wave_row_lo + off));
+      if (need_mask) {
+        const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key > lim) s[kb][r] = -INFINITY;
+          }
+      }
+
+      // Online softmax update for this lane's row.
+      float mx = s[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_new = fmaxf(m_run, mx * scale_log2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
+          s[kb][r] = p;
+          rs += p;
+        }
+      l_run = alpha * l_run + rs;
+      if (wave_any(alpha != 1.f)) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
+      }
+
+      // P (bf16) as the B operand of o^T += V^T P^T, 16 keys per MFMA.
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[kb][8 * s2 + 2 * e], s[kb][8 * s2 + 2 * e + 1]);
+          pb[kb][s2] = __builtin_bit_cast(bf16x8, w);
+        }
+
+      const int src = lane & 15;
+      const int tr_r = src >> 2;
+      const int tr_c = src & 3;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int n0 = 32 * nb + 16 * (li >> 4);
+        const int col = n0 + 4 * tr_c;
+        const int chunk = col >> 3;
+        const int sub = col & 7;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int r1 = 32 * kb + 16 * s2 + 4 * hh + tr_r;
+            const int r2 = r1 + 8;
+            const s16x4 lo = lds_read_tr(Vs + r1 * D + ((chunk ^ swz<CH>(r1)) * 8) + sub);
+            const s16x4 hi = lds_read_tr(Vs + r2 * D + ((chunk ^ swz<CH>(r2)) * 8) + sub);
+            o[nb] = mfma32(join_tr(lo, hi), pb[kb][s2], o[nb]);
+          }
+      }
+    }
+
+    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: one division per row, O in bf16, LSE in natural log.
+  const float l_tot = l_run + swap_halves(l_run);
+  if (qrow < Nq) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    __bf16* dst = Op + (size_t)qrow * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int n = 32 * nb + 8 * r4 + 4 * hh;
+        u32x2 w;
+        w[0] = pack_bf16x2(o[nb][4 * r4 + 0] * inv, o[nb][4 * r4 + 1] * inv);
+        w[1] = pack_bf16x2(o[nb][4 * r4 + 2] * inv, o[nb][4 * r4 + 3] * inv);
+        *(u32x2*)(dst + n) = w;
+      }
+    if (hh == 0) Lp[qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// fp32 path: the same tiling on v_mfma_f32_32x32x2f32 (P stays fp32).
+// One wave = 32 query rows, 32-key tiles.  Lane (i = l%32, h = l/32) holds
+// query row i; k-step 4*kk + t pairs lane half h with d = 8*kk + 4*h + t, so
+// K and Q operands come from one 16-byte read per four k-steps.
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int B, int H, int Hkv, int Nq, int Nk,
+    float scale_log2, int n_qtiles) {
+  constexpr int NT = NW * 64;
+  constexpr int BR = NW * 32;
+  constexpr int BC = 32;
+  constexpr int CH = D / 4;   // 16-byte chunks per fp32 row
+  constexpr int NLOAD = BC * CH / NT;
+  constexpr int KK = D / 8;   // 16-byte groups of k-steps
+  constexpr int NB = D / 32;
+  static_assert(BC * CH % NT == 0, "tile load split");
+
+  __shared__ __attribute__((aligned(16))) float smem[2][BC * D];  // [K|V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 31;
+  const int hh = lane >> 5;
+
+  const int BH = B * H;
+  const int wg = blockIdx.x;
+  const int qt = n_qtiles - 1 - wg / BH;
+  const int bh = wg % BH;
+  const int b = bh / H;
+  const int h = bh % H;
+  const int g = h / (H / Hkv);
+  const int q0 = qt * BR;
+  const int off = Nk - Nq;
+
+  const float* Qp = Q + ((size_t)b * H + h) * (size_t)Nq * D;
+  const float* Kp = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+  const float* Vp = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+  float* Op = O + ((size_t)b * H + h) * (size_t)Nq * D;
+  float* Lp = LSE + ((size_t)b * H + h) * (size_t)Nq;
+
+  const int qrow = q0 + wave * 32 + li;
+  int n_tiles;
+  if (CAUSAL) {
+    int last = min(Nk - 1, q0 + BR - 1 + off);
+    n_tiles = last < 0 ? 0 : last / BC + 1;
+  } else {
+    n_tiles = (Nk + BC - 1) / BC;
+  }
+
+  f32x4 qf[KK];
+  {
+    const bool ok = qrow < Nq;
+    const float* src = Qp + (size_t)(ok ? qrow : 0) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = ok ? *(const f32x4*)(src + 8 * kk + 4 * hh) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  f32x16 o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int k0 = t * BC;
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < NLOAD; ++it) {
+      const int cid = tid + it * NT;
+      const int row = cid / CH;
+      const int c = cid % CH;
+      const int key = k0 + row;
+      f32x4 kv = f32x4{0.f, 0.f, 0.f, 0.f}, vv = kv;
+      if (key < Nk) {
+        kv = *(const f32x4*)(Kp + (size_t)key * D + c * 4);
+        vv = *(const f32x4*)(Vp + (size_t)key * D + c * 4);
+      }
+      *(f32x4*)(&smem[0][row * D + ((c ^ (row & (CH - 1))) * 4)]) = kv;
+      *(f32x4*)(&smem[1][row * D + c * 4]) = vv;
+    }
+    __syncthreads();
+
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int c = 2 * kk + hh;
+      const f32x4 a = *(const f32x4*)(&smem[0][li * D + ((c ^ (li & (CH - 1))) * 4)]);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) s = mfma32_f32(a[tt], qf[kk][tt], s);
+    }
+    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > q0 + wave * 32 + off));
+    if (need_mask) {
+      const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key > lim) s[r] = -INFINITY;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -m_use));
+      s[r] = p;
+      rs += p;
+    }
+    l_run = alpha * l_run + rs;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+        const float a = smem[1][key * D + 32 * nb + li];
+        o[nb] = mfma32_f32(a, s[r], o[nb]);
+      }
+  }
+
+  const float l_tot = l_run + swap_halves(l_run);
+  if (qrow < Nq) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* dst = Op + (size_t)qrow * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int n = 32 * nb + 8 * r4 + 4 * hh;
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = o[nb][4 * r4 + e] * inv;
+        *(f32x4*)(dst + n) = w;
+      }
+    if (hh == 0) Lp[qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bf16(const FwdArgs& a, int nw, hipStream_t stream) {
+  const int br = nw * 32;
+  const int n_qtiles = (a.Nq + br - 1) / br;
+  dim3 grid((unsigned)(n_qtiles * a.B * a.H));
+  const float sl2 = a.scale * kLog2e;
+  if (nw == 4) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), grid, dim3(256), 0, stream,
+                       (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
+                       a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles);
+  } else {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 2>), grid, dim3(128), 0, stream,
+                       (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
+                       a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles);
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_f32(const FwdArgs& a, hipStream_t stream) {
+  constexpr int NW = 4;
+  const int n_qtiles = (a.Nq + NW * 32 - 1) / (NW * 32);
+  dim3 grid((unsigned)(n_qtiles * a.B * a.H));
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, NW>), grid, dim3(NW * 64), 0, stream,
+                     (const float*)a.Q, (const float*)a.K, (const float*)a.V, (float*)a.O, a.LSE,
+                     a.B, a.H, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qtiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
+  if (a.dtype_bf16) {
+    if (a.d == 128)
+      return a.causal ? launch_bf16<128, true>(a, p.waves, stream)
+                      : launch_bf16<128, false>(a, p.waves, stream);
+    return a.causal ? launch_bf16<64, true>(a, p.waves, stream)
+                    : launch_bf16<64, false>(a, p.waves, stream);
+  }
+  if (a.d == 128)
+    return a.causal ? launch_f32<128, true>(a, stream) : launch_f32<128, false>(a, stream);
+  return a.causal ? launch_f32<64, true>(a, stream) : launch_f32<64, false>(a, stream);
+}
+
+}  // namespace eta

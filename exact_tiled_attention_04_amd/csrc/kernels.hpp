@@ -1,0 +1,70 @@
+// Internal interface between the C-ABI host layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace eta {
+
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* LSE;
+  int B, H, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  bool dtype_bf16;
+};
+
+struct FwdPlan {
+  int waves;        // waves per workgroup (32 query rows each)
+  int block_rows;   // query rows per workgroup
+  int block_keys;   // keys per K/V tile
+  long long workgroups;
+};
+
+struct DecodeArgs {
+  const void* Q;
+  const void* K_cache;
+  const void* V_cache;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  void* O;
+  float* LSE;
+  int num_seqs, Hq, Hkv, d, block_size, num_blocks, max_blocks_per_seq, max_context;
+  int64_t block_stride, token_stride, head_stride;
+  float scale;
+  void* workspace;
+};
+
+struct DecodePlan {
+  int chunk_tokens;
+  int n_chunks_max;
+};
+
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* LSE;
+  void* dQ;
+  void* dK;
+  void* dV;
+  int B, H, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  void* workspace;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+size_t decode_workspace_bytes(int num_seqs, int Hq, int d, int n_chunks_max);
+size_t bwd_workspace_bytes(int B, int H, int Nq, int d);
+
+}  // namespace eta

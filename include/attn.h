@@ -1,0 +1,179 @@
+/*
+ * attn.h -- C ABI of the exact tiled attention library for AMD Instinct
+ * MI355X (gfx950).  Library file: libeta_attn.so.
+ *
+ * The library computes exact scaled-dot-product attention
+ *     O = softmax(scale * Q K^T + mask) V
+ * tile by tile with the online-softmax recurrence (running max, running sum,
+ * unnormalised accumulator, one division at the end), so the score and
+ * probability matrices never reach device memory.  Sources, cited by page
+ * title and section:
+ *   "Modern attention kernels" (blog.ecitis.org): "Standard attention
+ *     materializes quadratic state" (the formula, Nq and Nk), "Online softmax
+ *     makes tiling exact", "Kernel structure" (tiles, causal skipping),
+ *     "Backward pass recomputes scores", "Work partitioning in
+ *     FlashAttention-2", "Prefill and decode need different kernels", "Paged
+ *     attention changes addressing", "Failure modes" (page-table mismatch).
+ *   "Attention kernels" (inference.tusharamrit.in): online-softmax
+ *     derivation, FlashDecoding split-context merge, grouped-query sharing.
+ *   "Flash attention and IO-aware attention" (aigrafen.se): backward saves
+ *     only the row statistics.
+ *
+ * Common conventions
+ *   - Every pointer argument except `buf`/`stream` is a DEVICE pointer to
+ *     memory the caller owns; the library keeps no state between calls and
+ *     never allocates device memory.  Scratch memory is passed in through
+ *     `workspace`, sized by the matching *_workspace_size query.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; results are valid once the caller has
+ *     synchronised the stream.  Calls are reentrant.
+ *   - Tensors are contiguous and row-major with the head dimension fastest:
+ *     Q, O, dQ, dO: [B, H, Nq, d]; K, V, dK, dV: [B, Hkv, Nk, d];
+ *     LSE: [B, H, Nq] float32.  All tensor pointers must be 16-byte aligned.
+ *   - dtype ATTN_DTYPE_BF16: Q/K/V/O/dQ/dK/dV/dO are bfloat16, accumulation
+ *     is float32, outputs are rounded to nearest even.  ATTN_DTYPE_F32: all
+ *     float32 (forward only).
+ *   - Head dimension d must be 64 or 128.  H must be a multiple of Hkv; query
+ *     head h reads KV head h / (H / Hkv) (contiguous groups).
+ *   - causal != 0 applies the causal mask aligned to the bottom-right corner:
+ *     query row i may see key j iff j <= i + (Nk - Nq).  A row that sees no
+ *     key gets O = 0 and LSE = -inf.
+ *   - LSE is the natural-log log-sum-exp of the row's scaled, masked scores:
+ *     LSE = m + ln(l).  It is the only statistic the backward needs.
+ *   - Errors: arguments are validated on the host BEFORE anything is
+ *     enqueued; a failed validation returns its status and launches nothing.
+ *     ATTN_ERR_HIP reports a failed launch (hipGetLastError).  Data-dependent
+ *     device errors cannot be reported.  attn_last_error() returns a
+ *     human-readable detail of the last failure on the calling thread.
+ */
+#ifndef ETA_ATTN_H
+#define ETA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, inconsistent strides */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (e.g. d=96) */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query */
+  ATTN_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} attn_status_t;
+
+typedef enum { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype_t;
+
+typedef enum { ATTN_PHASE_FWD = 0, ATTN_PHASE_DECODE = 1, ATTN_PHASE_BWD = 2 } attn_phase_t;
+
+/*
+ * Forward (prefill) attention.  "Modern attention kernels", "Standard
+ * attention materializes quadratic state" defines S = Q K^T * scale,
+ * P = softmax(S), O = P V for Nq queries and Nk keys; "Kernel structure"
+ * gives the tiled loop and the causal tile skipping.
+ *   Q [B,H,Nq,d], K and V [B,Hkv,Nk,d]  (inputs, device, dtype)
+ *   O [B,H,Nq,d]                         (output, device, dtype)
+ *   LSE [B,H,Nq]                         (output, device, float32; may not be NULL)
+ *   B, H, Hkv, Nq, Nk >= 1; d in {64, 128}; scale > 0 and finite.
+ * Returns ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED or ATTN_ERR_HIP.
+ */
+attn_status_t attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                       int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                       attn_dtype_t dtype, void* stream);
+
+/*
+ * Bytes of workspace attn_decode_paged needs for these sizes (0 when the
+ * arguments are invalid).  chunk_tokens as for attn_decode_paged.
+ */
+size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_context,
+                                        int chunk_tokens);
+
+/*
+ * Single-query (decode) attention over a paged KV cache with grouped-query
+ * heads and a split-context merge.  "Modern attention kernels", "Prefill and
+ * decode need different kernels" and "Paged attention changes addressing":
+ * token position pos of sequence s lives in physical block
+ * block_table[s, pos / block_size] at slot pos % block_size; "Attention
+ * kernels", FlashDecoding: the context is split into chunks whose partial
+ * (o, m, l) are merged by max-rescaling.
+ *   Q            [num_seqs, Hq, d]                 device, bf16
+ *   K_cache, V_cache: element (blk, slot, kvh, c) at
+ *                blk*block_stride + slot*token_stride + kvh*head_stride + c
+ *                (strides in ELEMENTS; c contiguous), num_blocks blocks.
+ *                The default layout [num_blocks, block_size, Hkv, d] has
+ *                head_stride = d, token_stride = Hkv*d,
+ *                block_stride = block_size*Hkv*d.
+ *   block_table  [num_seqs, max_blocks_per_seq] int32, device.  Entries of
+ *                live tokens must lie in [0, num_blocks); a live token whose
+ *                entry does not is skipped (it gets probability 0) so a
+ *                page-table mismatch cannot read outside the cache.
+ *   context_lens [num_seqs] int32, device.  Tokens 0..ctx-1 are attended;
+ *                ctx <= 0 gives O = 0, LSE = -inf; ctx > max_context is
+ *                treated as max_context.  Cache slots past ctx (in the last
+ *                page) are never read into the result, whatever they hold.
+ *   O            [num_seqs, Hq, d] bf16 output; LSE [num_seqs, Hq] float32
+ *                output or NULL.
+ *   max_context  upper bound on context_lens (sizes the grid without reading
+ *                device memory); must be <= max_blocks_per_seq*block_size.
+ *   chunk_tokens context chunk per parallel work item, a positive multiple
+ *                of 32, or 0 to let the library choose.
+ *   Hq % Hkv == 0 and Hq / Hkv <= 16; d in {64, 128}; dtype must be BF16;
+ *   block_size >= 1; the strides must describe non-overlapping rows:
+ *   head_stride >= d, token_stride >= Hkv*head_stride,
+ *   block_stride >= block_size*token_stride, all multiples of 8.
+ *   workspace    device scratch of at least
+ *                attn_decode_paged_workspace_size(...) bytes, 16-byte aligned.
+ */
+attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache,
+                                const int32_t* block_table, const int32_t* context_lens, void* O,
+                                float* LSE, int num_seqs, int Hq, int Hkv, int d, int block_size,
+                                int num_blocks, int max_blocks_per_seq, int max_context,
+                                int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                                float scale, attn_dtype_t dtype, int chunk_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_bwd needs (fp32 dQ accumulator + row term D). */
+size_t attn_bwd_workspace_size(int B, int H, int Nq, int d);
+
+/*
+ * Backward of attn_fwd by recomputation: "Modern attention kernels",
+ * "Backward pass recomputes scores"; "Flash attention and IO-aware
+ * attention", backward paragraph (only the row statistics are saved).
+ *   Q, K, V, O, dO, LSE: as produced/consumed by attn_fwd (O and LSE must be
+ *   the forward's outputs for these Q, K, V, scale and causal).
+ *   dQ [B,H,Nq,d], dK and dV [B,Hkv,Nk,d]: outputs (bf16).  For Hkv < H the
+ *   KV gradients are summed over the query heads of each group.
+ *   dtype must be BF16; d in {64, 128}.
+ *   workspace: at least attn_bwd_workspace_size(B, H, Nq, d) bytes,
+ *   16-byte aligned.  dQ accumulates with float atomics, so its bits may
+ *   differ from run to run within rounding; dK and dV are deterministic.
+ */
+attn_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                       const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv,
+                       int Nq, int Nk, int d, float scale, int causal, attn_dtype_t dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Describe the kernel choice for a phase and shape ("Modern attention
+ * kernels", "Prefill and decode need different kernels": record the kernel
+ * choice separately per phase).  For ATTN_PHASE_DECODE, Nq is ignored, Nk is
+ * max_context, B is num_seqs and H is Hq.  Writes a NUL-terminated string of
+ * at most len bytes into buf (host memory) and returns the length it needed
+ * (excluding the NUL), or -1 on invalid arguments.
+ */
+int attn_plan_describe(int phase, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                       attn_dtype_t dtype, char* buf, size_t len);
+
+/* Static string naming a status code. */
+const char* attn_status_string(attn_status_t status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ETA_ATTN_H */

@@ -1,0 +1,148 @@
+"""C-ABI boundary checks that need no GPU.
+
+Every call here fails host-side validation (or is a pure host query), so no
+kernel is ever launched: the fake pointers below are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_04_amd import attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+FAKE = ctypes.c_void_p(1 << 20)        # aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
+NULL = ctypes.c_void_p(0)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return attn.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(attn.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "ATTN_OK"), (1, "ATTN_ERR_INVALID_ARG"), (2, "ATTN_ERR_UNSUPPORTED"),
+                       (3, "ATTN_ERR_WORKSPACE"), (4, "ATTN_ERR_HIP")]:
+        assert attn.attn_status_string(code) == name
+
+
+def _fwd(lib, q=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.125,
+         causal=1, dtype=attn.ATTN_DTYPE_BF16):
+    return lib.attn_fwd(q, FAKE, FAKE, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, dtype, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), attn.ATTN_ERR_INVALID_ARG),
+    (dict(lse=NULL), attn.ATTN_ERR_INVALID_ARG),
+    (dict(o=MISALIGNED), attn.ATTN_ERR_INVALID_ARG),
+    (dict(B=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Nq=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Nk=-3), attn.ATTN_ERR_INVALID_ARG),
+    (dict(H=3, Hkv=2), attn.ATTN_ERR_INVALID_ARG),
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(scale=0.0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=-1.0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), attn.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=7), attn.ATTN_ERR_INVALID_ARG),
+])
+def test_fwd_validation(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def _decode(lib, q=FAKE, ws=FAKE, ws_bytes=1 << 30, num_seqs=2, Hq=8, Hkv=2, d=128,
+            block_size=16, num_blocks=10, max_blocks=4, max_context=64, strides=None,
+            scale=0.1, dtype=attn.ATTN_DTYPE_BF16, chunk=0, lse=FAKE):
+    if strides is None:
+        strides = (block_size * Hkv * d, Hkv * d, d)
+    return lib.attn_decode_paged(q, FAKE, FAKE, FAKE, FAKE, FAKE, lse, num_seqs, Hq, Hkv, d,
+                                 block_size, num_blocks, max_blocks, max_context, strides[0],
+                                 strides[1], strides[2], scale, dtype, chunk, ws, ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), attn.ATTN_ERR_INVALID_ARG),
+    (dict(num_seqs=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=34, Hkv=2), attn.ATTN_ERR_UNSUPPORTED),   # 17 query heads per KV head
+    (dict(d=80), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(max_context=65), attn.ATTN_ERR_INVALID_ARG),  # beyond 4 blocks x 16
+    (dict(chunk=48), attn.ATTN_ERR_INVALID_ARG),
+    (dict(strides=(16 * 2 * 128, 128, 128)), attn.ATTN_ERR_INVALID_ARG),   # token stride < Hkv*d
+    (dict(strides=(2 * 128, 2 * 128, 128)), attn.ATTN_ERR_INVALID_ARG),    # block stride too small
+    (dict(strides=(16 * 2 * 132, 2 * 132, 130)), attn.ATTN_ERR_INVALID_ARG),  # unaligned head stride
+    (dict(dtype=attn.ATTN_DTYPE_F32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=NULL), attn.ATTN_ERR_WORKSPACE),
+    (dict(ws_bytes=16), attn.ATTN_ERR_WORKSPACE),
+    (dict(scale=float("inf")), attn.ATTN_ERR_INVALID_ARG),
+])
+def test_decode_validation(lib, kw, status):
+    assert _decode(lib, **kw) == status
+
+
+def _bwd(lib, ws=FAKE, ws_bytes=1 << 30, dtype=attn.ATTN_DTYPE_BF16, d=128, dq=FAKE, H=4, Hkv=2):
+    return lib.attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, 1, H, Hkv, 16, 16, d,
+                        0.1, 1, dtype, ws, ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=NULL), attn.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=attn.ATTN_DTYPE_F32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=NULL), attn.ATTN_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), attn.ATTN_ERR_WORKSPACE),
+    (dict(H=3, Hkv=2), attn.ATTN_ERR_INVALID_ARG),
+])
+def test_bwd_validation(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
+def test_workspace_queries(lib):
+    # Backward: fp32 dQ accumulator plus one float per row.
+    assert attn.attn_bwd_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 129 * 4
+    assert attn.attn_bwd_workspace_size(1, 1, 1, 96) == 0
+    # Decode: (d + 2) floats per (chunk, sequence, query head).
+    assert attn.attn_decode_paged_workspace_size(4, 8, 128, 1000, 256) == 4 * 4 * 8 * 130 * 4
+    assert attn.attn_decode_paged_workspace_size(4, 8, 128, 1000, 48) == 0
+    # The automatic chunk never needs more than the query reports.
+    auto = attn.attn_decode_paged_workspace_size(64, 32, 128, 32768, 0)
+    assert auto > 0
+
+
+def test_plan_describe_per_phase(lib):
+    fwd = attn.attn_plan_describe(attn.ATTN_PHASE_FWD, 1, 32, 32, 8192, 8192, 128, True)
+    assert "phase=fwd" in fwd and "Br=128" in fwd and "grid=2048" in fwd
+    small = attn.attn_plan_describe(attn.ATTN_PHASE_FWD, 1, 4, 4, 8192, 8192, 128, True)
+    assert "Br=64" in small  # too few workgroups at Br=128: split the sequence finer
+    dec = attn.attn_plan_describe(attn.ATTN_PHASE_DECODE, 64, 32, 8, 1, 32768, 128, False)
+    assert "phase=decode" in dec and "G=4" in dec
+    bwd = attn.attn_plan_describe(attn.ATTN_PHASE_BWD, 2, 16, 16, 4096, 4096, 128, True)
+    assert "phase=bwd" in bwd
+    with pytest.raises(ValueError):
+        attn.attn_plan_describe(attn.ATTN_PHASE_FWD, 1, 3, 2, 8, 8, 64, True)
+
+
+def test_tensor_marshalling_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.attn_fwd(q, q, q, 0.125, True)

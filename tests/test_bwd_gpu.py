@@ -1,0 +1,86 @@
+"""Backward parity: HIP recompute backward against the fp64 oracle's gradients."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_tiled_attention_04_amd import attn, workloads
+from parity import check_grad, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def _fwd_bwd(gpu, q, k, v, do, scale, causal):
+    qg, kg, vg, dog = (t.to(gpu) for t in (q, k, v, do))
+    o, lse = attn.attn_fwd(qg, kg, vg, scale, causal)
+    dq, dk, dv = attn.attn_bwd(qg, kg, vg, o, dog, lse, scale, causal)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d,causal", [
+    (1, 2, 2, 64, 64, 64, True),
+    (1, 2, 2, 128, 128, 128, False),
+    (2, 2, 2, 200, 200, 128, True),     # ragged query and key tiles
+    (1, 1, 1, 1, 1, 64, True),
+    (1, 2, 2, 17, 300, 64, True),      # Nq < Nk, bottom-right causal
+    (1, 2, 2, 300, 17, 128, False),
+    (1, 2, 2, 129, 100, 64, True),     # Nq > Nk: rows that see no key
+    (1, 4, 2, 257, 257, 128, True),    # grouped-query heads
+    (1, 8, 1, 96, 96, 64, False),
+])
+def test_bwd_small(gpu, B, H, Hkv, Nq, Nk, d, causal):
+    q, k, v, do = workloads.backward(B, H, Hkv, Nq, Nk, d, dtype="bf16", seed=Nq * 7 + Nk)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = _fwd_bwd(gpu, q, k, v, do, scale, causal)
+    rq, rk, rv = oracle.backward(to64(q), to64(k), to64(v), to64(do), scale, causal)
+    check_grad(to64(dq), rq, "dQ")
+    check_grad(to64(dk), rk, "dK")
+    check_grad(to64(dv), rv, "dV")
+
+
+def test_bwd_large_logits(gpu):
+    """Queries scaled by 6: dK (linear in Q) reaches |21|, so the bound is
+    magnitude-aware (bf16 output rounding alone exceeds 5e-2 there)."""
+    q, k, v, do = workloads.backward(1, 2, 2, 300, 300, 128, dtype="bf16", seed=21)
+    q = (q.float() * 6.0).to(torch.bfloat16)
+    dq, dk, dv = _fwd_bwd(gpu, q, k, v, do, 1 / math.sqrt(128), True)
+    rq, rk, rv = oracle.backward(to64(q), to64(k), to64(v), to64(do), 1 / math.sqrt(128), True)
+    check_grad(to64(dq), rq, "dQ", magnitude_aware=True)
+    check_grad(to64(dk), rk, "dK", magnitude_aware=True)
+    check_grad(to64(dv), rv, "dV", magnitude_aware=True)
+
+
+def test_bwd_dk_dv_deterministic(gpu):
+    q, k, v, do = workloads.backward(1, 4, 4, 333, 333, 128, dtype="bf16", seed=22)
+    a = _fwd_bwd(gpu, q, k, v, do, 0.09, True)
+    b = _fwd_bwd(gpu, q, k, v, do, 0.09, True)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    assert (a[0].float() - b[0].float()).abs().max().item() <= 1e-2
+
+
+def test_causal_bwd_b2_h16_n4096_d128(gpu):
+    """B=2, H=16, N=4096, d=128, causal, scale 1/sqrt(128): full-size launch.
+    Two whole heads against the oracle; on every head the invariants
+    sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 (rows of P sum to one, rows of
+    dS sum to zero)."""
+    B, H, N, d = 2, 16, 4096, 128
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, do = workloads.backward(B, H, H, N, N, d, dtype="bf16", seed=0)
+    dq, dk, dv = _fwd_bwd(gpu, q, k, v, do, scale, True)
+    for b, h in [(0, 0), (1, H - 1)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = oracle.backward(to64(q[sl]), to64(k[sl]), to64(v[sl]), to64(do[sl]),
+                                     scale, True)
+        check_grad(to64(dq[sl]), rq, f"dQ[{b},{h}]")
+        check_grad(to64(dk[sl]), rk, f"dK[{b},{h}]")
+        check_grad(to64(dv[sl]), rv, f"dV[{b},{h}]")
+    sdv = to64(dv).sum(axis=2)
+    sdo = to64(do).sum(axis=2)
+    # bf16 outputs: each of the N summed terms carries ~2^-9 relative rounding.
+    assert np.abs(sdv - sdo).max() <= 0.5, np.abs(sdv - sdo).max()
+    assert np.abs(to64(dk).sum(axis=2)).max() <= 0.5
+    assert torch.isfinite(dq.float()).all()
