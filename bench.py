@@ -1,0 +1,256 @@
+"""Benchmark of the exact tiled attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over synthetic inputs already
+resident in HBM:
+  1. causal bf16 forward, B=1, H=32, N=8192, d=128, scale 1/sqrt(128)
+     (the headline workload: TFLOP/s and fraction of dense bf16 MFMA peak);
+  2. paged GQA decode, 64 sequences, Hq=32, Hkv=8, d=128, contexts uniform
+     in [4096, 32768], 16-token pages via a seeded permutation (KV GB/s and
+     fraction of HBM peak);
+  3. causal bf16 backward, B=2, H=16, N=4096, d=128 (TFLOP/s).
+Each call is bracketed by HIP events recorded on the stream the library
+launches on (torch's current stream); the K timed steps are bracketed by a
+device synchronisation on both sides.  Rank 0 prints one JSON line.
+
+FLOPs follow "Attention kernels" (the FLOPs paragraph): 4 N^2 d per head,
+halved under the causal mask; the backward also reports its algorithmic
+five-product count 10 N^2 d / 2.  Decode bytes are the K and V cache rows the
+contexts cover: 2 * sum(ctx) * Hkv * d * 2 bytes.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "fwd attention TFLOP/s & % bf16 MFMA peak; paged decode KV GB/s % HBM peak"
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the fp64 oracle on the host (profiling runs)")
+    ap.add_argument("--cpu-heads", type=int, default=24,
+                    help="heads of the forward workload the oracle is timed on")
+    return ap.parse_args()
+
+
+def _source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel, sources, per_launch_algorithmic):
+    """HBM traffic per launch from the committed rocprofv3 PMC summary, when
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    rec = data.get(kernel)
+    if not rec or rec.get("source_digest") != _source_digest(sources):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this "
+              "build (the multi-GPU design is described, not built).", file=sys.stderr)
+        return 2
+
+    import torch
+    from exact_tiled_attention_04_amd import attn, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    attn.load_library()  # fails loudly when the HIP library is missing
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs (seeded, generated on the device, resident before timing)
+    fw = workloads.WORKLOADS["causal_bf16_b1_h32_n8192_d128"]
+    q, k, v = workloads.prefill(fw["B"], fw["H"], fw["Hkv"], fw["Nq"], fw["Nk"], fw["d"],
+                                dtype="bf16", seed=fw["seed"], device=str(dev))
+    o = torch.empty_like(q)
+    lse = torch.empty((fw["B"], fw["H"], fw["Nq"]), dtype=torch.float32, device=dev)
+    fwd_flops = 4.0 * fw["B"] * fw["H"] * fw["Nq"] * fw["Nk"] * fw["d"] / 2.0
+
+    dw = workloads.WORKLOADS["paged_gqa_decode_bf16_s64_hq32_hkv8_d128"]
+    dec = workloads.decode(num_seqs=dw["num_seqs"], Hq=dw["Hq"], Hkv=dw["Hkv"], d=dw["d"],
+                           ctx_lo=dw["ctx_lo"], ctx_hi=dw["ctx_hi"], block_size=dw["block_size"],
+                           max_blocks_per_seq=dw["max_blocks_per_seq"], dtype="bf16",
+                           seed=dw["seed"], device=str(dev))
+    dbt = dec["block_table"].to(dev)
+    dctx = dec["context_lens"].to(dev)
+    dout = torch.empty_like(dec["q"])
+    dlse = torch.empty((dw["num_seqs"], dw["Hq"]), dtype=torch.float32, device=dev)
+    dws = torch.empty(max(attn.attn_decode_paged_workspace_size(
+        dw["num_seqs"], dw["Hq"], dw["d"], dw["ctx_hi"], 0), 16), dtype=torch.uint8, device=dev)
+    sum_ctx = int(dec["context_lens"].sum())
+    dec_bytes = 2.0 * sum_ctx * dw["Hkv"] * dw["d"] * 2
+
+    bw = workloads.WORKLOADS["causal_bwd_bf16_b2_h16_n4096_d128"]
+    bq, bk, bv, bdo = workloads.backward(bw["B"], bw["H"], bw["Hkv"], bw["Nq"], bw["Nk"], bw["d"],
+                                         dtype="bf16", seed=bw["seed"], device=str(dev))
+    bo, blse = attn.attn_fwd(bq, bk, bv, bw["scale"], True)
+    bdq, bdk, bdv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
+    bws = torch.empty(attn.attn_bwd_workspace_size(bw["B"], bw["H"], bw["Nq"], bw["d"]),
+                      dtype=torch.uint8, device=dev)
+    bwd_flops_fwd_equiv = 4.0 * bw["B"] * bw["H"] * bw["Nq"] * bw["Nk"] * bw["d"] / 2.0
+    bwd_flops_algo = 2.5 * bwd_flops_fwd_equiv
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        e = events
+        if e: e[0].record(stream)
+        attn.attn_fwd(q, k, v, fw["scale"], True, out=o, lse=lse, stream=stream)
+        if e: e[1].record(stream)
+        attn.attn_decode_paged(dec["q"], dec["k_cache"], dec["v_cache"], dbt, dctx, dw["scale"],
+                               dw["ctx_hi"], out=dout, lse=dlse, workspace=dws, stream=stream)
+        if e: e[2].record(stream)
+        attn.attn_bwd(bq, bk, bv, bo, bdo, blse, bw["scale"], True, dq=bdq, dk=bdk, dv=bdv,
+                      workspace=bws, stream=stream)
+        if e: e[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def med(vals):
+        s = sorted(vals)
+        return s[len(s) // 2]
+
+    fwd_ms = [ev[0].elapsed_time(ev[1]) for ev in events]
+    dec_ms = [ev[1].elapsed_time(ev[2]) for ev in events]
+    bwd_ms = [ev[2].elapsed_time(ev[3]) for ev in events]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    fwd_tflops = fwd_flops / (fwd_avg * 1e-3) / 1e12
+    dec_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
+    bwd_tflops_algo = bwd_flops_algo / (bwd_avg * 1e-3) / 1e12
+    bwd_tflops_fwd_equiv = bwd_flops_fwd_equiv / (bwd_avg * 1e-3) / 1e12
+
+    fwd_src = ["exact_tiled_attention_04_amd/csrc/fwd.hip",
+               "exact_tiled_attention_04_amd/csrc/common.hpp"]
+    dec_src = ["exact_tiled_attention_04_amd/csrc/decode.hip",
+               "exact_tiled_attention_04_amd/csrc/common.hpp"]
+    result = {
+        "metric": METRIC,
+        "value": round(fwd_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal_bf16_b1_h32_n8192_d128 (headline) + "
+                        "paged_gqa_decode_bf16_s64_hq32_hkv8_d128 + causal_bwd_bf16_b2_h16_n4096_d128",
+            "B": fw["B"], "H": fw["H"], "N": fw["Nq"], "d": fw["d"], "causal": True,
+            "plan": attn.attn_plan_describe(attn.ATTN_PHASE_FWD, fw["B"], fw["H"], fw["Hkv"],
+                                            fw["Nq"], fw["Nk"], fw["d"], True),
+        },
+        "roofline": {
+            "kernel": "fwd_bf16_kernel<128,causal,4>",
+            "bound": "mfma",
+            "achieved": round(fwd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": _traffic("fwd_bf16_kernel<128,causal,4>", fwd_src, None),
+            "avg_launch_ms": round(fwd_avg, 4),
+            "algorithmic_flop_per_launch": fwd_flops,
+        },
+        "decode": {
+            "value": round(dec_gbs, 1),
+            "unit": "GB/s",
+            "frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "avg_call_ms": round(dec_avg, 4),
+            "kv_bytes_per_call": dec_bytes,
+            "sum_context_tokens": sum_ctx,
+            "plan": attn.attn_plan_describe(attn.ATTN_PHASE_DECODE, dw["num_seqs"], dw["Hq"],
+                                            dw["Hkv"], 1, dw["ctx_hi"], dw["d"], False),
+            "roofline": {"kernel": "decode_split_kernel<128>+decode_merge_kernel", "bound": "hbm",
+                         "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                         "traffic": _traffic("decode_split_kernel<128>", dec_src, None)},
+        },
+        "bwd": {
+            "value": round(bwd_tflops_algo, 2),
+            "unit": "TFLOP/s (5-product algorithmic count)",
+            "fwd_equivalent_tflops": round(bwd_tflops_fwd_equiv, 2),
+            "frac_mfma_peak": round(bwd_tflops_algo / PEAK_BF16_TFLOPS, 4),
+            "avg_call_ms": round(bwd_avg, 4),
+        },
+        "per_call_ms_median": {"fwd": round(med(fwd_ms), 4), "decode": round(med(dec_ms), 4),
+                               "bwd": round(med(bwd_ms), 4)},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(q, k, v, fw, args.cpu_heads)
+    print(json.dumps(result))
+    return 0
+
+
+def cpu_baseline(q, k, v, fw, heads):
+    """The fp64 oracle, as it stands, timed on the host over a bounded sample:
+    `heads` of the forward workload's heads, scaled to TFLOP/s with the same
+    per-head FLOP count the GPU figure uses."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    qs = q[:, :heads].float().cpu().numpy().astype(np.float64)
+    ks = k[:, :heads].float().cpu().numpy().astype(np.float64)
+    vs = v[:, :heads].float().cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.forward(qs, ks, vs, fw["scale"], True)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * heads * fw["Nq"] * fw["Nk"] * fw["d"] / 2.0
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{heads} of {fw['H']} heads of causal_bf16_b1_h32_n8192_d128 "
+                  f"(fp64 numpy, materialised S and P), {dt:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())
