@@ -43,6 +43,9 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the fp64 oracle on the host (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 512 MiB device copy first, so PMC byte counters "
+                         "can be scaled against a kernel of known traffic")
     ap.add_argument("--cpu-heads", type=int, default=24,
                     help="heads of the forward workload the oracle is timed on")
     return ap.parse_args()
@@ -86,6 +89,13 @@ def main():
     attn.load_library()  # fails loudly when the HIP library is missing
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        # 512 MiB read + 512 MiB written by one copy kernel.
+        src = torch.ones(256 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- inputs (seeded, generated on the device, resident before timing)
     fw = workloads.WORKLOADS["causal_bf16_b1_h32_n8192_d128"]

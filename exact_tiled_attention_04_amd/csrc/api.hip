@@ -77,15 +77,16 @@ attn_status_t check_fwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, floa
 
 int plan_decode_chunk(int num_seqs, int Hkv, int max_context, int chunk_tokens) {
   if (chunk_tokens > 0) return chunk_tokens;
-  // Aim for about 32 waves per CU over the whole launch when every sequence
-  // is as long as max_context: enough independent K/V streams in flight to
-  // cover HBM latency, few enough partials that the merge stays small.
-  const long long target_units = 32LL * kNumCU;
+  // About 128 split waves per CU if every sequence were max_context long
+  // (about half that for contexts spread uniformly below it): many short,
+  // independent K/V streams keep HBM busy, while the partials stay a few
+  // percent of the cache bytes.  Chunks are multiples of 32 tokens.
+  const long long target_units = 128LL * kNumCU;
   const long long pairs = (long long)num_seqs * Hkv;
   long long chunk = (pairs * (long long)max_context + target_units - 1) / target_units;
   chunk = (chunk + 31) / 32 * 32;
-  if (chunk < 256) chunk = 256;
-  if (chunk > 8192) chunk = 8192;
+  if (chunk < 64) chunk = 64;
+  if (chunk > 4096) chunk = 4096;
   return (int)chunk;
 }
 

@@ -77,11 +77,6 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ d
   *(u32x4*)(dQ + 8 * i) = w;
 }
 
-template <int CH>
-__device__ __forceinline__ int swz(int row) {
-  return row & (CH - 1);
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_main_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -131,7 +126,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(
     const int c = cid % CH;
     const int key = j0 + row;
     u32x4 v = key < Nk ? *(const u32x4*)(Kp + (size_t)key * D + 8 * c) : u32x4{0, 0, 0, 0};
-    *(u32x4*)(Ks + row * D + ((c ^ swz<CH>(row)) * 8)) = v;
+    *(u32x4*)(Ks + row * D + ((c ^ tile_swz<D>(row)) * 8)) = v;
   }
   // This wave's keys as B operands: lane (j = li, hh) holds X[j][16 ks + 8 hh + e].
   const int jw = j0 + 32 * w + li;
@@ -208,7 +203,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(
       const int cid = tid + 256 * it;
       const int row = cid / CH;
       const int c = cid % CH;
-      const int idx = row * D + ((c ^ swz<CH>(row)) * 8);
+      const int idx = row * D + ((c ^ tile_swz<D>(row)) * 8);
       *(u32x4*)(qd + idx) = rq[it];
       *(u32x4*)(dd + idx) = rdo[it];
     }
@@ -240,7 +235,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(
       const int row = 32 * qb + li;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int idx = row * D + (((2 * ks + hh) ^ swz<CH>(row)) * 8);
+        const int idx = row * D + (((2 * ks + hh) ^ tile_swz<D>(row)) * 8);
         s = mfma32(*(const bf16x8*)(qs + idx), kf[ks], s);
         dp = mfma32(*(const bf16x8*)(ds + idx), vf[ks], dp);
       }
@@ -283,7 +278,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(
         u32x2 v;
         v[0] = pack_bf16x2(dp[4 * r4 + 0], dp[4 * r4 + 1]);
         v[1] = pack_bf16x2(dp[4 * r4 + 2], dp[4 * r4 + 3]);
-        *(u32x2*)(dSt + krow * kBQ + ((chunk ^ (krow & (DSCH - 1))) * 8) + (qc & 7)) = v;
+        *(u32x2*)(dSt + krow * kBQ + ((chunk ^ tile_swz<kBQ>(krow)) * 8) + (qc & 7)) = v;
       }
     }
 
@@ -299,8 +294,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(
         for (int s2 = 0; s2 < 2; ++s2) {
           const int r1 = 32 * qb + 16 * s2 + 4 * hh + tr_r;
           const int r2 = r1 + 8;
-          const int a1 = r1 * D + ((chunk ^ swz<CH>(r1)) * 8) + sub;
-          const int a2 = r2 * D + ((chunk ^ swz<CH>(r2)) * 8) + sub;
+          const int a1 = r1 * D + ((chunk ^ tile_swz<D>(r1)) * 8) + sub;
+          const int a2 = r2 * D + ((chunk ^ tile_swz<D>(r2)) * 8) + sub;
           const bf16x8 dot = join_tr(lds_read_tr(ds + a1), lds_read_tr(ds + a2));
           const bf16x8 qtt = join_tr(lds_read_tr(qs + a1), lds_read_tr(qs + a2));
           dv[nb] = mfma32(dot, pb[qb][s2], dv[nb]);
@@ -328,19 +323,23 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(
         for (int kj = 0; kj < kBK / 16; ++kj) {
           const int r1 = 16 * kj + 4 * hh + tr_r;
           const int r2 = r1 + 8;
-          const bf16x8 kt_op = join_tr(lds_read_tr(Ks + r1 * D + ((nchunk ^ swz<CH>(r1)) * 8) + nsub),
-                                       lds_read_tr(Ks + r2 * D + ((nchunk ^ swz<CH>(r2)) * 8) + nsub));
+          // A = (scale dS)[i][j] (rows = queries), B = K[j][n]: both column
+          // reads of row-major LDS tiles.
           const bf16x8 ds_op =
-              join_tr(lds_read_tr(dSt + r1 * kBQ + ((ichunk ^ (r1 & (DSCH - 1))) * 8) + isub),
-                      lds_read_tr(dSt + r2 * kBQ + ((ichunk ^ (r2 & (DSCH - 1))) * 8) + isub));
-          acc = mfma32(kt_op, ds_op, acc);
+              join_tr(lds_read_tr(dSt + r1 * kBQ + ((ichunk ^ tile_swz<kBQ>(r1)) * 8) + isub),
+                      lds_read_tr(dSt + r2 * kBQ + ((ichunk ^ tile_swz<kBQ>(r2)) * 8) + isub));
+          const bf16x8 k_op = join_tr(lds_read_tr(Ks + r1 * D + ((nchunk ^ tile_swz<D>(r1)) * 8) + nsub),
+                                      lds_read_tr(Ks + r2 * D + ((nchunk ^ tile_swz<D>(r2)) * 8) + nsub));
+          acc = mfma32(ds_op, k_op, acc);
         }
-        // Lane (query 32 qb + li, hh) register r holds column 32 cs + 8 (r/4) + 4 hh + r%4.
-        const int q = q0 + 32 * qb + li;
-        if (q < Nq) {
-          float* dst = dq_acc + (hb + q) * D + 32 * cs + 4 * hh;
+        // Lane (column 32 cs + li, hh) register r holds query row
+        // 32 qb + 8 (r/4) + 4 hh + r%4: each atomic instruction covers two
+        // contiguous 128-byte row segments.
+        float* dst = dq_acc + (hb + q0 + 32 * qb + 4 * hh) * D + 32 * cs + li;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + 8 * (r >> 2) + (r & 3), acc[r]);
+        for (int r = 0; r < 16; ++r) {
+          const int qi = 8 * (r >> 2) + (r & 3);
+          if (q0 + 32 * qb + 4 * hh + qi < Nq) unsafeAtomicAdd(dst + (size_t)qi * D, acc[r]);
         }
       }
     }

@@ -78,6 +78,35 @@ __device__ __forceinline__ bf16x8 join_tr(const s16x4& lo, const s16x4& hi) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// XOR swizzles of the 16-byte chunks of row-major bf16 tiles in LDS (64 banks
+// of 4 bytes; a b128 access is served 16 lanes per cycle, a b64 transpose
+// read 32 lanes per cycle).  The tiles are read two ways:
+//   * row reads (MFMA A operand, ds_read_b128): lanes 0..15 read the same
+//     chunk of 16 consecutive rows;
+//   * transpose reads (ds_read_b64_tr_b16): 32 lanes read 4 consecutive rows,
+//     64 contiguous bytes each.
+// tile_swz<D> keeps both conflict-free for rows of D bf16:
+//   D = 128 (256-byte rows): the two 2-bit halves of row % 16 swapped, so 16
+//     consecutive rows land on 16 distinct chunks and 4 consecutive rows on 4
+//     distinct 64-byte groups;
+//   D = 64 (128-byte rows, two rows per bank line): row bit 1 moves to chunk
+//     bit 2 and row bits 2..3 to chunk bits 0..1, so rows of equal parity
+//     among 16 take 8 distinct chunks and rows r, r + 2 differ in chunk bit 2.
+template <int D>
+__device__ __forceinline__ int tile_swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Swizzle of the decode V tile, read only by transposes whose 32 lanes cover
+// 8 consecutive rows at the same 32-byte column: the 8 rows must fall on 8
+// distinct chunk pairs (D = 128) or, for rows of equal parity, 4 (D = 64).
+template <int D>
+__device__ __forceinline__ int decode_swz(int row) {
+  if constexpr (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+  else return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+}
+
 // Value of lane (l ^ 32): the other half of the wave.
 __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);

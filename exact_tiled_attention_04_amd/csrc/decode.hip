@@ -33,8 +33,15 @@ namespace {
 
 constexpr int kTok = 32;  // tokens per inner step (two 16-token pages)
 
-template <int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(
+// Two waves per SIMD (eight per CU), each with the next 32 tokens' K and V
+// in flight: enough bytes outstanding to cover HBM latency without spills.
+#ifndef ETA_DECODE_WAVES_PER_EU
+#define ETA_DECODE_WAVES_PER_EU 2
+#endif
+
+template <int D, bool PAGE16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETA_DECODE_WAVES_PER_EU)))
+void decode_split_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc, const __bf16* __restrict__ Vc,
     const int* __restrict__ block_table, const int* __restrict__ ctx_lens,
     float* __restrict__ part_o, float* __restrict__ part_ml, int num_seqs, int Hq, int Hkv,
@@ -91,13 +98,34 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     return base + (size_t)physical * block_stride + (size_t)offset * token_stride;
   };
 
-  u32x4 kr[2][KS], vr[VL];
-  u32x4 kn[2][KS], vn[VL];
+  // Physical block of the 16-token page starting at pos0 (a multiple of 16),
+  // or -1 when the page lies past the chunk or its entry is outside the cache.
+  // pos0 is wave-uniform, so this is a scalar load.
+  auto page_phys = [&](int pos0) -> int {
+    if (pos0 >= t_end) return -1;
+    const int ph = bt[pos0 >> 4];
+    return (ph >= 0 && ph < num_blocks) ? ph : -1;
+  };
+
+  u32x4 kr[2][KS], kn[2][KS], vr[VL];
   unsigned long long live_r[2], live_n[2];  // ballot: bit qc of word pp = token t0+16pp+qc is live
-  auto load_step = [&](int t0, u32x4 (&kd)[2][KS], u32x4 (&vd)[VL], unsigned long long (&live)[2]) {
+  auto load_k = [&](int t0, u32x4 (&kd)[2][KS], unsigned long long (&live)[2]) {
+    int ph[2] = {0, 0};
+    if (PAGE16) {
+      ph[0] = page_phys(t0);
+      ph[1] = page_phys(t0 + 16);
+    }
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
-      const __bf16* p = tok_ptr(Kg, t0 + 16 * pp + qc);
+      const __bf16* p;
+      if (PAGE16) {
+        const int pos = t0 + 16 * pp + qc;
+        p = (ph[pp] >= 0 && pos < t_end)
+                ? Kg + (size_t)ph[pp] * block_stride + (size_t)qc * token_stride
+                : nullptr;
+      } else {
+        p = tok_ptr(Kg, t0 + 16 * pp + qc);
+      }
       live[pp] = __ballot(p != nullptr);
       if (p) {
 #pragma unroll
@@ -107,13 +135,28 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         for (int ks = 0; ks < KS; ++ks) kd[pp][ks] = u32x4{0, 0, 0, 0};
       }
     }
+  };
+  auto load_v = [&](int t0) {
+    int ph[2] = {0, 0};
+    if (PAGE16) {
+      ph[0] = page_phys(t0);
+      ph[1] = page_phys(t0 + 16);
+    }
 #pragma unroll
     for (int it = 0; it < VL; ++it) {
       const int cid = lane + 64 * it;
       const int tk = cid / CH;
       const int c = cid % CH;
-      const __bf16* p = tok_ptr(Vg, t0 + tk);
-      vd[it] = p ? *(const u32x4*)(p + 8 * c) : u32x4{0, 0, 0, 0};
+      const __bf16* p;
+      if (PAGE16) {
+        const int pp = tk >> 4;
+        p = (ph[pp] >= 0 && t0 + tk < t_end)
+                ? Vg + (size_t)ph[pp] * block_stride + (size_t)(tk & 15) * token_stride
+                : nullptr;
+      } else {
+        p = tok_ptr(Vg, t0 + tk);
+      }
+      vr[it] = p ? *(const u32x4*)(p + 8 * c) : u32x4{0, 0, 0, 0};
     }
   };
 
@@ -122,15 +165,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  auto compute_step = [&](u32x4 (&kd)[2][KS], u32x4 (&vd)[VL], unsigned long long (&live)[2]) {
-    // Stage V rows (row-major, 16-byte chunks XOR-swizzled by row).
+  // V rows of the current step into the wave's LDS tile (row-major,
+  // 16-byte chunks XOR-swizzled by row); frees vr for the next step's loads.
+  auto stage_v = [&]() {
 #pragma unroll
     for (int it = 0; it < VL; ++it) {
       const int cid = lane + 64 * it;
       const int tk = cid / CH;
       const int c = cid % CH;
-      *(u32x4*)(vs + tk * D + ((c ^ (tk & (CH - 1))) * 8)) = vd[it];
+      *(u32x4*)(vs + tk * D + ((c ^ decode_swz<D>(tk)) * 8)) = vr[it];
     }
+  };
+  auto compute_step = [&](u32x4 (&kd)[2][KS], unsigned long long (&live)[2]) {
     f32x4 sc[2];
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
@@ -183,26 +229,38 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       const int col = 16 * nb + 4 * tr_c;
       const int chunk8 = col >> 3;
       const int sub = col & 7;
-      const s16x4 lo = lds_read_tr(vs + r1 * D + ((chunk8 ^ (r1 & (CH - 1))) * 8) + sub);
-      const s16x4 hi = lds_read_tr(vs + r2 * D + ((chunk8 ^ (r2 & (CH - 1))) * 8) + sub);
+      const s16x4 lo = lds_read_tr(vs + r1 * D + ((chunk8 ^ decode_swz<D>(r1)) * 8) + sub);
+      const s16x4 hi = lds_read_tr(vs + r2 * D + ((chunk8 ^ decode_swz<D>(r2)) * 8) + sub);
       o[nb] = mfma16(join_tr(lo, hi), pb, o[nb]);
     }
     // The next step's LDS writes must follow these reads.
     __asm__ volatile("" ::: "memory");
   };
 
+  // Software pipeline: V of the current step is staged in LDS before the
+  // next step's K and V loads are issued, so they fly during the compute.
   int t0 = t_begin;
-  load_step(t0, kr, vr, live_r);
+  load_k(t0, kr, live_r);
+  load_v(t0);
   while (true) {
-    const int t1 = t0 + kTok;
-    if (t1 < t_end) load_step(t1, kn, vn, live_n);
-    compute_step(kr, vr, live_r);
+    stage_v();
+    int t1 = t0 + kTok;
+    if (t1 < t_end) {
+      load_v(t1);
+      load_k(t1, kn, live_n);
+    }
+    compute_step(kr, live_r);
     if (t1 >= t_end) break;
-    const int t2 = t1 + kTok;
-    if (t2 < t_end) load_step(t2, kr, vr, live_r);
-    compute_step(kn, vn, live_n);
-    if (t2 >= t_end) break;
-    t0 = t2;
+    t0 = t1;
+    stage_v();
+    t1 = t0 + kTok;
+    if (t1 < t_end) {
+      load_v(t1);
+      load_k(t1, kr, live_r);
+    }
+    compute_step(kn, live_n);
+    if (t1 >= t_end) break;
+    t0 = t1;
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
@@ -255,7 +313,8 @@ hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t
   if (p.n_chunks_max > 0) {
     const int units = p.n_chunks_max * a.Hkv;
     dim3 grid((unsigned)((units + 3) / 4), (unsigned)a.num_seqs);
-    hipLaunchKernelGGL((decode_split_kernel<D>), grid, dim3(256), 0, stream,
+    auto kern = a.block_size == 16 ? decode_split_kernel<D, true> : decode_split_kernel<D, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream,
                        (const __bf16*)a.Q, (const __bf16*)a.K_cache, (const __bf16*)a.V_cache,
                        a.block_table, a.context_lens, part_o, part_ml, a.num_seqs, a.Hq, a.Hkv,
                        a.Hq / a.Hkv, a.block_size, a.num_blocks, a.max_blocks_per_seq,

@@ -33,15 +33,14 @@ namespace {
 
 constexpr int kBC = 64;  // keys per K/V tile
 
-// XOR swizzle of 16-byte chunks within an LDS row (removes bank conflicts of
-// the column-of-rows access patterns).  CH = chunks per row.
-template <int CH>
-__device__ __forceinline__ int swz(int row) {
-  return row & (CH - 1);
-}
+// Two waves per SIMD: the softmax of one wave overlaps the MFMAs of the other.
+#ifndef ETA_FWD_WAVES_PER_EU
+#define ETA_FWD_WAVES_PER_EU 2
+#endif
 
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ETA_FWD_WAVES_PER_EU)))
+void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
     int B, int H, int Hkv, int Nq, int Nk, float scale_log2, int n_qtiles) {
@@ -131,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
       const int cid = tid + it * NT;
       const int row = cid / CH;
       const int c = cid % CH;
-      const int idx = row * D + ((c ^ swz<CH>(row)) * 8);
+      const int idx = row * D + ((c ^ tile_swz<D>(row)) * 8);
       *(u32x4*)(&smem[buf][0][idx]) = pk[it];
       *(u32x4*)(&smem[buf][1][idx]) = pv[it];
     }
@@ -160,7 +159,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
         const int row = 32 * kb + li;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *(const bf16x8*)(Ks + row * D + (((2 * ks + hh) ^ swz<CH>(row)) * 8));
+          const bf16x8 a = *(const bf16x8*)(Ks + row * D + (((2 * ks + hh) ^ tile_swz<D>(row)) * 8));
           s[kb] = mfma32(a, qf[ks], s[kb]);
         }
       }
@@ -233,8 +232,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
           for (int s2 = 0; s2 < 2; ++s2) {
             const int r1 = 32 * kb + 16 * s2 + 4 * hh + tr_r;
             const int r2 = r1 + 8;
-            const s16x4 lo = lds_read_tr(Vs + r1 * D + ((chunk ^ swz<CH>(r1)) * 8) + sub);
-            const s16x4 hi = lds_read_tr(Vs + r2 * D + ((chunk ^ swz<CH>(r2)) * 8) + sub);
+            const s16x4 lo = lds_read_tr(Vs + r1 * D + ((chunk ^ tile_swz<D>(r1)) * 8) + sub);
+            const s16x4 hi = lds_read_tr(Vs + r2 * D + ((chunk ^ tile_swz<D>(r2)) * 8) + sub);
             o[nb] = mfma32(join_tr(lo, hi), pb[kb][s2], o[nb]);
           }
       }
