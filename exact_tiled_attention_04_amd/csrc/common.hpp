@@ -62,9 +62,10 @@ __device__ __forceinline__ float bf16_bits_to_float(unsigned short h) {
 }
 
 // LDS transpose read of 4 bf16 (see header comment for the lane mapping).
+// The pointer is cast straight to the LDS address space (not through an
+// integer) so alias analysis still sees which LDS object it reads.
 __device__ __forceinline__ s16x4 lds_read_tr(const void* lds_ptr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)((__attribute__((address_space(3))) char*)(size_t)lds_ptr));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_ptr);
 }
 
 __device__ __forceinline__ bf16x8 join_tr(const s16x4& lo, const s16x4& hi) {
@@ -111,6 +112,51 @@ __device__ __forceinline__ int decode_swz(int row) {
 __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
+
+// v_permlane32_swap: exchanges lanes 32..63 of `a` with lanes 0..31 of `b`.
+// Starting from a = b = x it leaves a = [x_lo | x_lo], b = [x_hi | x_hi], so
+// every lane holds both x[l] and x[l ^ 32].  Written as inline assembly with
+// both registers as outputs (the compiler builtin drops the second result);
+// the s_nops cover the VALU-write / permlane-read hazards on either side.
+__device__ __forceinline__ void permlane32_swap(unsigned& a, unsigned& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+// max / sum of lanes l and l ^ 32 without an LDS round trip.
+__device__ __forceinline__ float halves_max(float x) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+  permlane32_swap(a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+  permlane32_swap(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zeros and stores past it are dropped, so ragged tiles need no branches.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(buf_rsrc r, int voffset, int soffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0));
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane l's bytes land at lds_base + 16 * l (lds_base wave-uniform); lanes
+// whose offset is past the buffer range write zeros (both verified on gfx950).
+// Completion is tracked by vmcnt, not lgkmcnt.
+__device__ __forceinline__ void buf_load16_lds(buf_rsrc r, void* lds_base, int voffset,
+                                               int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base,
+                                           16, voffset, soffset, 0, 0);
+}
+
+// Wait until every vector-memory operation of this wave (including direct
+// LDS copies) has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 

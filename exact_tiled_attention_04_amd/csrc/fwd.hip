@@ -18,8 +18,11 @@
 //     registers (packed to bf16), V^T read from the row-major V tile in LDS
 //     with ds_read_b64_tr_b16;
 //   * the softmax runs in base 2 with scale*log2(e) folded into one FMA;
-//   * K/V tiles are double-buffered in LDS with a register prefetch of the
-//     next tile, one barrier per tile;
+//   * K/V tiles are double-buffered in LDS and filled by direct
+//     global->LDS buffer copies issued one tile ahead (rows past the end
+//     arrive as zeros), one barrier per tile;
+//   * the row max is exchanged between half-waves with v_permlane32_swap,
+//     and the accumulator is rescaled only when the reference max moves;
 //   * grid = batch x head x query tile ("Work partitioning in
 //     FlashAttention-2": parallel over the sequence), causal tiles heaviest
 //     first, consecutive workgroups on different heads so that each XCD's L2
@@ -38,6 +41,13 @@ constexpr int kBC = 64;  // keys per K/V tile
 #define ETA_FWD_WAVES_PER_EU 2
 #endif
 
+// The running maximum is a reference point, not necessarily the exact row
+// maximum: it moves (and the accumulator is rescaled) only when a tile's
+// maximum exceeds it by more than kSlack in base-2 units.  o / l and
+// m + log2 l are the same for any reference point, so the result is exact as
+// with a per-tile rescale, while exponents stay <= 2^kSlack.
+constexpr float kSlack = 8.f;
+
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ETA_FWD_WAVES_PER_EU)))
 void fwd_bf16_kernel(
@@ -50,15 +60,22 @@ void fwd_bf16_kernel(
   constexpr int NLOAD = kBC * CH / NT;       // 16-byte loads per thread per tile
   constexpr int KS = D / 16;                 // k-steps of the QK^T product
   constexpr int NB = D / 32;                 // 32-wide column blocks of o
+  constexpr int ROW = D * 2;                 // bytes per row
+  constexpr int TILE = kBC * ROW;            // bytes per K (or V) tile
   static_assert(kBC * CH % NT == 0, "tile load split");
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][kBC * D];  // [buf][K|V]
+  // Two LDS buffers (K tile then V tile each) as separate objects, so the
+  // direct copies into one are known not to alias reads of the other.
+  __shared__ __attribute__((aligned(16))) char smem0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) char smem1[2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int li = lane & 31;   // query row within the wave / A-row
   const int hh = lane >> 5;   // half-wave
+  const int tr_r = (lane & 15) >> 2;
+  const int tr_c = lane & 3;
 
   const int BH = B * H;
   const int wg = blockIdx.x;
@@ -70,9 +87,9 @@ void fwd_bf16_kernel(
   const int q0 = qt * BR;
   const int off = Nk - Nq;  // bottom-right causal alignment
 
-  const __bf16* Qp = Q + ((size_t)b * H + h) * (size_t)Nq * D;
-  const __bf16* Kp = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
-  const __bf16* Vp = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+  const buf_rsrc qrs = make_rsrc(Q + ((size_t)b * H + h) * (size_t)Nq * D, (unsigned)Nq * ROW);
+  const buf_rsrc krs = make_rsrc(K + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
+  const buf_rsrc vrs = make_rsrc(V + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
   __bf16* Op = O + ((size_t)b * H + h) * (size_t)Nq * D;
   float* Lp = LSE + ((size_t)b * H + h) * (size_t)Nq;
 
@@ -88,80 +105,66 @@ void fwd_bf16_kernel(
     n_tiles = (Nk + kBC - 1) / kBC;
   }
 
-  // Queries of this lane's row as the B operand (Q^T), zero past Nq.
+  // Queries of this lane's row as the B operand (Q^T); rows past Nq read 0.
   bf16x8 qf[KS];
-  {
-    const bool ok = qrow < Nq;
-    const __bf16* src = Qp + (size_t)(ok ? qrow : 0) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = ok ? *(const u32x4*)(src + 16 * ks + 8 * hh) : u32x4{0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(qrs, qrow * ROW + (16 * ks + 8 * hh) * 2, 0));
+
+  // Direct copies: instruction `it` of this wave fills 16-byte LDS slots
+  // p = (wave * NLOAD + it) * 64 + lane of a tile, i.e. row p / CH and
+  // swizzled chunk p % CH; the lane loads the logical chunk that belongs there.
+  int goff[NLOAD];
+#pragma unroll
+  for (int it = 0; it < NLOAD; ++it) {
+    const int p = (wave * NLOAD + it) * 64 + lane;
+    const int row = p / CH;
+    const int c = (p % CH) ^ tile_swz<D>(row);
+    goff[it] = row * ROW + c * 16;
   }
+  int kofs[KS];   // K row (32 kb + li), chunk 2 ks + hh
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kofs[ks] = li * ROW + (((2 * ks + hh) ^ tile_swz<D>(li)) * 16);
+  int vofs[NB][2];  // V transpose reads: rows 4 hh + tr_r (+8), columns 32 nb + 16 (li/16) + 4 tr_c
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int rr = 4 * hh + tr_r + 8 * hf;
+      const int col = 32 * nb + 16 * (li >> 4) + 4 * tr_c;
+      vofs[nb][hf] = rr * ROW + (((col >> 3) ^ tile_swz<D>(rr)) * 16) + (col & 7) * 2;
+    }
 
   f32x16 o[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) o[nb] = f32x16{};
-  float m_run = -INFINITY;  // running max, base-2 units (scores * scale * log2 e)
+  float m_run = -INFINITY;  // reference max, base-2 units (scores * scale * log2 e)
   float l_run = 0.f;        // this lane's partial running sum
 
-  u32x4 pk[NLOAD], pv[NLOAD];
-  auto load_tile = [&](int t) {
-    const int k0 = t * kBC;
+  auto load_tile = [&](int t, char* dst) {
+    const int soff = t * TILE;  // rows past Nk arrive as zeros (buffer range)
 #pragma unroll
     for (int it = 0; it < NLOAD; ++it) {
-      const int cid = tid + it * NT;
-      const int row = cid / CH;
-      const int c = cid % CH;
-      const int key = k0 + row;
-      if (key < Nk) {
-        pk[it] = *(const u32x4*)(Kp + (size_t)key * D + c * 8);
-        pv[it] = *(const u32x4*)(Vp + (size_t)key * D + c * 8);
-      } else {
-        pk[it] = u32x4{0, 0, 0, 0};
-        pv[it] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < NLOAD; ++it) {
-      const int cid = tid + it * NT;
-      const int row = cid / CH;
-      const int c = cid % CH;
-      const int idx = row * D + ((c ^ tile_swz<D>(row)) * 8);
-      *(u32x4*)(&smem[buf][0][idx]) = pk[it];
-      *(u32x4*)(&smem[buf][1][idx]) = pv[it];
+      char* slot = dst + (wave * NLOAD + it) * 1024;
+      buf_load16_lds(krs, slot, goff[it], soff);
+      buf_load16_lds(vrs, slot + TILE, goff[it], soff);
     }
   };
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  auto step = [&](int t, const char* Ks, char* next) {
     const int k0 = t * kBC;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-
+    if (t + 1 < n_tiles) load_tile(t + 1, next);
     // Tiles wholly above this wave's diagonal contribute nothing.
     const bool wave_live = !CAUSAL || (k0 <= wave_row_lo + 31 + off);
     if (wave_live) {
-      const __bf16* Ks = smem[buf][0];
-      const __bf16* Vs = smem[buf][1];
+      const char* Vs = Ks + TILE;
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = f32x16{};
-        const int row = 32 * kb + li;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *(const bf16x8*)(Ks + row * D + (((2 * ks + hh) ^ tile_swz<D>(row)) * 8));
-          s[kb] = mfma32(a, qf[ks], s[kb]);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+          s[kb] = mfma32(*(const bf16x8*)(Ks + kb * 32 * ROW + kofs[ks]), qf[ks], s[kb]);
       }
 
       // Mask the causal boundary and the ragged key tail.
@@ -183,11 +186,18 @@ void fwd_bf16_kernel(
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
+      const float mx2 = halves_max(mx) * scale_log2;
+      if (wave_any(mx2 > m_run + kSlack)) {
+        const float m_new = fmaxf(m_run, mx2);
+        const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -197,13 +207,7 @@ void fwd_bf16_kernel(
           s[kb][r] = p;
           rs += p;
         }
-      l_run = alpha * l_run + rs;
-      if (wave_any(alpha != 1.f)) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
-      }
+      l_run += rs;
 
       // P (bf16) as the B operand of o^T += V^T P^T, 16 keys per MFMA.
       bf16x8 pb[2][2];
@@ -216,35 +220,33 @@ void fwd_bf16_kernel(
           for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[kb][8 * s2 + 2 * e], s[kb][8 * s2 + 2 * e + 1]);
           pb[kb][s2] = __builtin_bit_cast(bf16x8, w);
         }
-
-      const int src = lane & 15;
-      const int tr_r = src >> 2;
-      const int tr_c = src & 3;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int n0 = 32 * nb + 16 * (li >> 4);
-        const int col = n0 + 4 * tr_c;
-        const int chunk = col >> 3;
-        const int sub = col & 7;
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
-            const int r1 = 32 * kb + 16 * s2 + 4 * hh + tr_r;
-            const int r2 = r1 + 8;
-            const s16x4 lo = lds_read_tr(Vs + r1 * D + ((chunk ^ tile_swz<D>(r1)) * 8) + sub);
-            const s16x4 hi = lds_read_tr(Vs + r2 * D + ((chunk ^ tile_swz<D>(r2)) * 8) + sub);
+            const char* vb = Vs + (32 * kb + 16 * s2) * ROW;
+            const s16x4 lo = lds_read_tr(vb + vofs[nb][0]);
+            const s16x4 hi = lds_read_tr(vb + vofs[nb][1]);
             o[nb] = mfma32(join_tr(lo, hi), pb[kb][s2], o[nb]);
           }
-      }
     }
-
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    wait_vmem();
     __syncthreads();
+  };
+
+  if (n_tiles > 0) load_tile(0, smem0);
+  wait_vmem();
+  __syncthreads();
+  // Unrolled by two so each step's LDS buffers are fixed objects.
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, smem0, smem1);
+    if (t + 1 < n_tiles) step(t + 1, smem1, smem0);
   }
 
   // Epilogue: one division per row, O in bf16, LSE in natural log.
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = halves_sum(l_run);
   if (qrow < Nq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __bf16* dst = Op + (size_t)qrow * D;
