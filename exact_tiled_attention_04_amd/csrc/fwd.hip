@@ -48,6 +48,7 @@ constexpr int kBC = 64;  // keys per K/V tile
 // with a per-tile rescale, while exponents stay <= 2^kSlack.
 constexpr float kSlack = 8.f;
 
+
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ETA_FWD_WAVES_PER_EU)))
 void fwd_bf16_kernel(
@@ -71,7 +72,7 @@ void fwd_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 31;   // query row within the wave / A-row
   const int hh = lane >> 5;   // half-wave
   const int tr_r = (lane & 15) >> 2;
@@ -158,13 +159,22 @@ void fwd_bf16_kernel(
     const bool wave_live = !CAUSAL || (k0 <= wave_row_lo + 31 + off);
     if (wave_live) {
       const char* Vs = Ks + TILE;
-      f32x16 s[2];
+      // S^T for keys 0..31 (s[0]) and 32..63 (s[1]); the two accumulation
+      // chains interleave and each k-step's K operands are read one step ahead.
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      bf16x8 a0 = *(const bf16x8*)(Ks + kofs[0]);
+      bf16x8 a1 = *(const bf16x8*)(Ks + 32 * ROW + kofs[0]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[kb] = mfma32(*(const bf16x8*)(Ks + kb * 32 * ROW + kofs[ks]), qf[ks], s[kb]);
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 n0 = a0, n1 = a1;
+        if (ks + 1 < KS) {
+          n0 = *(const bf16x8*)(Ks + kofs[ks + 1]);
+          n1 = *(const bf16x8*)(Ks + 32 * ROW + kofs[ks + 1]);
+        }
+        s[0] = mfma32(a0, qf[ks], s[0]);
+        s[1] = mfma32(a1, qf[ks], s[1]);
+        a0 = n0;
+        a1 = n1;
       }
 
       // Mask the causal boundary and the ragged key tail.
@@ -220,17 +230,20 @@ void fwd_bf16_kernel(
           for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[kb][8 * s2 + 2 * e], s[kb][8 * s2 + 2 * e + 1]);
           pb[kb][s2] = __builtin_bit_cast(bf16x8, w);
         }
+      // o^T += V^T P^T: 4 MFMAs per 32-column block, V^T operands read one
+      // MFMA ahead.
+      auto vread = [&](int i) {
+        const int nb = i >> 2, kb = (i >> 1) & 1, s2 = i & 1;
+        const char* vb = Vs + (32 * kb + 16 * s2) * ROW;
+        return join_tr(lds_read_tr(vb + vofs[nb][0]), lds_read_tr(vb + vofs[nb][1]));
+      };
+      bf16x8 va = vread(0);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const char* vb = Vs + (32 * kb + 16 * s2) * ROW;
-            const s16x4 lo = lds_read_tr(vb + vofs[nb][0]);
-            const s16x4 hi = lds_read_tr(vb + vofs[nb][1]);
-            o[nb] = mfma32(join_tr(lo, hi), pb[kb][s2], o[nb]);
-          }
+      for (int i = 0; i < 4 * NB; ++i) {
+        const bf16x8 vn = (i + 1 < 4 * NB) ? vread(i + 1) : va;
+        o[i >> 2] = mfma32(va, pb[(i >> 1) & 1][i & 1], o[i >> 2]);
+        va = vn;
+      }
     }
     wait_vmem();
     __syncthreads();
