@@ -9,21 +9,29 @@
 //   D_i = sum_n dO_in O_in (= sum_j P_ij dP_ij), dS = P (dP - D),
 //   dQ = scale dS K, dK = scale dS^T Q.
 //
-// Kernels:
-//   bwd_pre:  D = rowsum(dO * O) in fp32, and zero the fp32 dQ accumulator
-//             (a fill kernel, no memset node).
-//   bwd_main: one workgroup per (batch, KV head, 128-key tile), four waves of
-//             32 keys each.  K and V stay in registers (and K in LDS); for
-//             every query head of the KV group and every 64-query tile that
-//             can see the keys, Q, dO, LSE and D are staged in LDS
-//             (double-buffered through registers).  Each wave computes
-//             S = Q K^T and dP = dO V^T with its keys along the lanes, forms
-//             P and dS, accumulates dV^T += dO^T P and dK^T += Q^T dS with
-//             the transposed operands read by ds_read_b64_tr_b16, then
-//             writes scale*dS^T to LDS; after a barrier the waves split
-//             dQ = (scale dS) K over all 128 keys into 32x32 blocks and add
-//             them to the fp32 accumulator with hardware float atomics.
-//   bwd_dq:   dQ fp32 accumulator -> bf16.
+// Kernels (no atomics; every output element has exactly one writer, so all
+// three gradients are deterministic):
+//   bwd_pre:  D = rowsum(dO * O) and LSE2 = LSE * log2(e) in fp32 (rows that
+//             see no key get LSE2 = +inf, hence P = 0).
+//   bwd_dkdv: one workgroup per (batch, KV head, 128-key tile), four waves of
+//             32 keys.  K and V of the wave's keys stay in registers; Q, dO,
+//             LSE2 and D of each 64-query tile that can see the keys (for
+//             every query head of the KV group) are copied straight into LDS,
+//             double-buffered.  Each wave forms S = Q K^T and dP = dO V^T with
+//             its keys along the lanes, then P and dS, and accumulates
+//             dV^T += dO^T P and dK^T += Q^T (scale dS) with the transposed
+//             operands read by ds_read_b64_tr_b16.
+//   bwd_dq:   one workgroup per (batch, head, 128-query tile), four waves of
+//             32 queries, laid out like the forward: S^T = K Q^T and
+//             dP^T = V dO^T with the queries along the lanes, then
+//             dQ^T += K^T (scale dS)^T with K^T read transposed from the same
+//             LDS tile.  K/V tiles arrive by direct copies, double-buffered.
+// The split costs two extra products (S and dP are formed in both kernels)
+// and buys the removal of the fp32 dQ accumulator and its atomics.
+//
+// Rows past Nq or Nk arrive as zeros from the buffer loads.  A zero query
+// row has dO = 0 and adds nothing to dK or dV, so the dK/dV kernel applies
+// only the causal mask; the dQ kernel also masks keys past Nk (see there).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,14 +39,24 @@ namespace eta {
 
 namespace {
 
-constexpr int kBK = 128;  // keys per workgroup (32 per wave)
-constexpr int kBQ = 64;   // queries per inner tile
+constexpr int kBK = 128;  // keys per dK/dV workgroup (32 per wave)
+constexpr int kBQ = 64;   // queries per dK/dV inner tile
+constexpr int kBC = 64;   // keys per dQ inner tile
+constexpr int kBR = 128;  // queries per dQ workgroup
+
+#ifndef ETA_BWD_KV_WAVES_PER_EU
+#define ETA_BWD_KV_WAVES_PER_EU 1
+#endif
+#ifndef ETA_BWD_Q_WAVES_PER_EU
+#define ETA_BWD_Q_WAVES_PER_EU 2
+#endif
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ O,
                                                       const __bf16* __restrict__ dO,
+                                                      const float* __restrict__ LSE,
                                                       float* __restrict__ Dsum,
-                                                      float* __restrict__ dq_acc, long long rows) {
+                                                      float* __restrict__ LSE2, long long rows) {
   constexpr int CH = D / 8;
   constexpr int RPB = 256 / CH;  // rows per block
   const int t = threadIdx.x;
@@ -53,103 +71,67 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
       acc += bf16_bits_to_float(a[e] & 0xffff) * bf16_bits_to_float(b[e] & 0xffff);
       acc += bf16_bits_to_float(a[e] >> 16) * bf16_bits_to_float(b[e] >> 16);
     }
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4*)(dq_acc + row * D + 8 * c) = z;
-    *(f32x4*)(dq_acc + row * D + 8 * c + 4) = z;
   }
 #pragma unroll
   for (int m = CH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && c == 0) Dsum[row] = acc;
+  if (row < rows && c == 0) {
+    Dsum[row] = acc;
+    const float l = LSE[row];
+    LSE2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ dq_acc,
-                                                     __bf16* __restrict__ dQ, long long n8) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *(const f32x4*)(dq_acc + 8 * i);
-  const f32x4 b = *(const f32x4*)(dq_acc + 8 * i + 4);
-  u32x4 w;
-  w[0] = pack_bf16x2(a[0], a[1]);
-  w[1] = pack_bf16x2(a[2], a[3]);
-  w[2] = pack_bf16x2(b[0], b[1]);
-  w[3] = pack_bf16x2(b[2], b[3]);
-  *(u32x4*)(dQ + 8 * i) = w;
-}
+// ----------------------------------------------------------------- dK, dV
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_main_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
-    float* __restrict__ dq_acc, __bf16* __restrict__ dK, __bf16* __restrict__ dV, int B, int H,
-    int Hkv, int Nq, int Nk, float scale, float scale_log2) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETA_BWD_KV_WAVES_PER_EU)))
+void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                     const float* __restrict__ LSE2, const float* __restrict__ Dsum,
+                     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int B, int H, int Hkv,
+                     int Nq, int Nk, float scale, float scale_log2) {
+  constexpr int NT = 256;
   constexpr int CH = D / 8;
   constexpr int KS = D / 16;
   constexpr int NB = D / 32;
-  constexpr int QLOAD = kBQ * CH / 256;  // 16-byte loads per thread per Q (or dO) tile
-  constexpr int KLOAD = kBK * CH / 256;
-  constexpr int DSCH = kBQ / 8;          // chunks per dS^T row
+  constexpr int ROW = D * 2;
+  constexpr int QT = kBQ * ROW;            // bytes of one Q (or dO) tile
+  constexpr int NLOAD = kBQ * CH / NT;     // direct copies per thread per tile
+  constexpr int STAT = 2 * QT;             // LSE2 then D, kBQ floats each
+  constexpr int BUF = STAT + 2 * kBQ * 4;
 
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  __bf16* Ks = (__bf16*)smem_raw;                       // [kBK][D]
-  __bf16* Qs = Ks + kBK * D;                            // [2][kBQ][D]
-  __bf16* dOs = Qs + 2 * kBQ * D;                       // [2][kBQ][D]
-  __bf16* dSt = dOs + 2 * kBQ * D;                      // [kBK][kBQ]
-  float* stat = (float*)(dSt + kBK * kBQ);              // [2][2][kBQ]: LSE2, D
+  __shared__ __attribute__((aligned(16))) char sm0[BUF];
+  __shared__ __attribute__((aligned(16))) char sm1[BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31;
   const int hh = lane >> 5;
-  const int src = lane & 15;
-  const int tr_r = src >> 2;
-  const int tr_c = src & 3;
+  const int tr_r = (lane & 15) >> 2;
+  const int tr_c = lane & 3;
 
-  const int n_kt = (Nk + kBK - 1) / kBK;
-  const int kt = blockIdx.x % n_kt;
-  const int bg = blockIdx.x / n_kt;
+  const int BG = B * Hkv;
+  const int kt = blockIdx.x / BG;  // key tiles seen by the most queries first
+  const int bg = blockIdx.x % BG;
   const int b = bg / Hkv;
   const int g = bg % Hkv;
   const int G = H / Hkv;
   const int j0 = kt * kBK;
   const int off = Nk - Nq;
 
-  const __bf16* Kp = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
-  const __bf16* Vp = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
-
-  // K tile into LDS (also the source of this wave's K fragment).
-#pragma unroll
-  for (int it = 0; it < KLOAD; ++it) {
-    const int cid = tid + 256 * it;
-    const int row = cid / CH;
-    const int c = cid % CH;
-    const int key = j0 + row;
-    u32x4 v = key < Nk ? *(const u32x4*)(Kp + (size_t)key * D + 8 * c) : u32x4{0, 0, 0, 0};
-    *(u32x4*)(Ks + row * D + ((c ^ tile_swz<D>(row)) * 8)) = v;
-  }
-  // This wave's keys as B operands: lane (j = li, hh) holds X[j][16 ks + 8 hh + e].
-  const int jw = j0 + 32 * w + li;
+  // This wave's 32 keys as B operands: lane (j = li, hh) holds X[j][16 ks + 8 hh + e].
+  const int jw = j0 + 32 * wave + li;
+  const buf_rsrc krs = make_rsrc(K + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
+  const buf_rsrc vrs = make_rsrc(V + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
   bf16x8 kf[KS], vf[KS];
-  {
-    const bool ok = jw < Nk;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 a = ok ? *(const u32x4*)(Kp + (size_t)jw * D + 16 * ks + 8 * hh) : u32x4{0, 0, 0, 0};
-      u32x4 v = ok ? *(const u32x4*)(Vp + (size_t)jw * D + 16 * ks + 8 * hh) : u32x4{0, 0, 0, 0};
-      kf[ks] = __builtin_bit_cast(bf16x8, a);
-      vf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(krs, jw * ROW + (16 * ks + 8 * hh) * 2, 0));
+    vf[ks] = __builtin_bit_cast(bf16x8, buf_load16(vrs, jw * ROW + (16 * ks + 8 * hh) * 2, 0));
   }
 
-  f32x16 dv[NB], dk[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    dv[nb] = f32x16{};
-    dk[nb] = f32x16{};
-  }
-
-  // Query tiles that can see this key tile.
+  // Query tiles that can see this key tile, for each head of the group.
   const int n_qt = (Nq + kBQ - 1) / kBQ;
   int qt_begin = 0;
   if (CAUSAL) {
@@ -159,85 +141,75 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(
   const int per_head = n_qt > qt_begin ? n_qt - qt_begin : 0;
   const int n_iter = per_head * G;
 
-  u32x4 rq[QLOAD], rdo[QLOAD];
-  float rstat = 0.f;
-  auto iter_coords = [&](int itx, int& h, int& q0) {
-    h = g * G + itx / per_head;
-    q0 = (qt_begin + itx % per_head) * kBQ;
-  };
-  auto load_q = [&](int itx) {
-    int h, q0;
-    iter_coords(itx, h, q0);
-    const size_t hb = ((size_t)b * H + h) * (size_t)Nq;
+  // Loop-invariant byte offsets (the same scheme as the forward).
+  int goff[NLOAD];
 #pragma unroll
-    for (int it = 0; it < QLOAD; ++it) {
-      const int cid = tid + 256 * it;
-      const int row = cid / CH;
-      const int c = cid % CH;
-      const int q = q0 + row;
-      if (q < Nq) {
-        rq[it] = *(const u32x4*)(Q + (hb + q) * D + 8 * c);
-        rdo[it] = *(const u32x4*)(dO + (hb + q) * D + 8 * c);
-      } else {
-        rq[it] = u32x4{0, 0, 0, 0};
-        rdo[it] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < 2 * kBQ) {
-      const int row = tid % kBQ;
-      const int q = q0 + row;
-      if (tid < kBQ) {
-        // LSE in base 2; rows past Nq or with no visible key give P = 0.
-        const float l = q < Nq ? LSE[hb + q] : -INFINITY;
-        rstat = l == -INFINITY ? INFINITY : l * kLog2e;
-      } else {
-        rstat = q < Nq ? Dsum[hb + q] : 0.f;
-      }
-    }
-  };
-  auto store_q = [&](int buf) {
-    __bf16* qd = Qs + buf * kBQ * D;
-    __bf16* dd = dOs + buf * kBQ * D;
-#pragma unroll
-    for (int it = 0; it < QLOAD; ++it) {
-      const int cid = tid + 256 * it;
-      const int row = cid / CH;
-      const int c = cid % CH;
-      const int idx = row * D + ((c ^ tile_swz<D>(row)) * 8);
-      *(u32x4*)(qd + idx) = rq[it];
-      *(u32x4*)(dd + idx) = rdo[it];
-    }
-    if (tid < 2 * kBQ) stat[buf * 2 * kBQ + tid] = rstat;
-  };
-
-  if (n_iter > 0) {
-    load_q(0);
-    store_q(0);
+  for (int it = 0; it < NLOAD; ++it) {
+    const int p = (wave * NLOAD + it) * 64 + lane;
+    const int row = p / CH;
+    goff[it] = row * ROW + (((p % CH) ^ tile_swz<D>(row)) * 16);
   }
-  __syncthreads();
+  int rofs[KS];  // row read: query row li of a 32-row block, chunk 2 ks + hh
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) rofs[ks] = li * ROW + (((2 * ks + hh) ^ tile_swz<D>(li)) * 16);
+  int tofs[NB][2];  // transpose read: rows 4 hh + tr_r (+8), columns 32 nb + 16 (li/16) + 4 tr_c
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int rr = 4 * hh + tr_r + 8 * hf;
+      const int col = 32 * nb + 16 * (li >> 4) + 4 * tr_c;
+      tofs[nb][hf] = rr * ROW + (((col >> 3) ^ tile_swz<D>(rr)) * 16) + (col & 7) * 2;
+    }
 
-  for (int itx = 0; itx < n_iter; ++itx) {
-    const int buf = itx & 1;
-    int h, q0;
-    iter_coords(itx, h, q0);
-    if (itx + 1 < n_iter) load_q(itx + 1);
-    const __bf16* qs = Qs + buf * kBQ * D;
-    const __bf16* ds = dOs + buf * kBQ * D;
-    const float* lse2 = stat + buf * 2 * kBQ;
+  f32x16 dv[NB], dk[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    dv[nb] = f32x16{};
+    dk[nb] = f32x16{};
+  }
+
+  auto load_tiles = [&](int itx, char* dst) {
+    const int h = g * G + itx / per_head;
+    const int q0 = (qt_begin + itx % per_head) * kBQ;
+    const size_t hb = ((size_t)b * H + h) * (size_t)Nq;
+    const buf_rsrc qrs = make_rsrc(Q + hb * D, (unsigned)Nq * ROW);
+    const buf_rsrc ors = make_rsrc(dO + hb * D, (unsigned)Nq * ROW);
+    const int soff = q0 * ROW;
+#pragma unroll
+    for (int it = 0; it < NLOAD; ++it) {
+      char* slot = dst + (wave * NLOAD + it) * 1024;
+      buf_load16_lds(qrs, slot, goff[it], soff);
+      buf_load16_lds(ors, slot + QT, goff[it], soff);
+    }
+    if (wave < 2) {
+      // kBQ floats of LSE2 (wave 0) or D (wave 1), 4 bytes per lane.
+      const buf_rsrc srs = make_rsrc((wave == 0 ? LSE2 : Dsum) + hb, (unsigned)Nq * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          srs, (__attribute__((address_space(3))) void*)(dst + STAT + wave * kBQ * 4), 4,
+          lane * 4, q0 * 4, 0, 0);
+    }
+  };
+
+  auto step = [&](int itx, const char* cur, char* next) {
+    const int q0 = (qt_begin + itx % per_head) * kBQ;
+    if (itx + 1 < n_iter) load_tiles(itx + 1, next);
+    const char* Qs = cur;
+    const char* Os = cur + QT;
+    const float* lse2 = (const float*)(cur + STAT);
     const float* dsum = lse2 + kBQ;
+    const bool need_mask = CAUSAL && (j0 + 32 * wave + 31 > q0 + off);
 
-    const bool need_mask =
-        (j0 + kBK > Nk) || (CAUSAL && (j0 + 32 * w + 31 > q0 + off));
     bf16x8 pb[2][2], sb[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 s = f32x16{}, dp = f32x16{};
-      const int row = 32 * qb + li;
+      const char* qrow = Qs + qb * 32 * ROW;
+      const char* orow = Os + qb * 32 * ROW;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int idx = row * D + (((2 * ks + hh) ^ tile_swz<D>(row)) * 8);
-        s = mfma32(*(const bf16x8*)(qs + idx), kf[ks], s);
-        dp = mfma32(*(const bf16x8*)(ds + idx), vf[ks], dp);
+        s = mfma32(*(const bf16x8*)(qrow + rofs[ks]), kf[ks], s);
+        dp = mfma32(*(const bf16x8*)(orow + rofs[ks]), vf[ks], dp);
       }
       // Lane (key jw, hh) register r holds query row q0 + 32 qb + 8 (r/4) + 4 hh + r%4.
 #pragma unroll
@@ -249,11 +221,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
           float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[e]));
-          if (need_mask) {
-            const int qrow = q0 + rloc + e;
-            const bool vis = (jw < Nk) && (!CAUSAL || jw <= qrow + off);
-            p = vis ? p : 0.f;
-          }
+          if (need_mask && jw > q0 + rloc + e + off) p = 0.f;
           s[r] = p;
           dp[r] = p * (dp[r] - d4[e]) * scale;
         }
@@ -269,86 +237,36 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(
         pb[qb][s2] = __builtin_bit_cast(bf16x8, wp);
         sb[qb][s2] = __builtin_bit_cast(bf16x8, wd);
       }
-      // scale*dS^T into LDS: row = key (32 w + li), 4 consecutive queries per store.
-      const int krow = 32 * w + li;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int qc = 32 * qb + 8 * r4 + 4 * hh;
-        const int chunk = qc >> 3;
-        u32x2 v;
-        v[0] = pack_bf16x2(dp[4 * r4 + 0], dp[4 * r4 + 1]);
-        v[1] = pack_bf16x2(dp[4 * r4 + 2], dp[4 * r4 + 3]);
-        *(u32x2*)(dSt + krow * kBQ + ((chunk ^ tile_swz<kBQ>(krow)) * 8) + (qc & 7)) = v;
-      }
     }
 
-    // dV^T += dO^T P and dK^T += Q^T (scale dS): transposed A operands via LDS tr reads.
+    // dV^T += dO^T P and dK^T += Q^T (scale dS).
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = 32 * nb + 16 * (li >> 4) + 4 * tr_c;
-      const int chunk = col >> 3;
-      const int sub = col & 7;
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const int r1 = 32 * qb + 16 * s2 + 4 * hh + tr_r;
-          const int r2 = r1 + 8;
-          const int a1 = r1 * D + ((chunk ^ tile_swz<D>(r1)) * 8) + sub;
-          const int a2 = r2 * D + ((chunk ^ tile_swz<D>(r2)) * 8) + sub;
-          const bf16x8 dot = join_tr(lds_read_tr(ds + a1), lds_read_tr(ds + a2));
-          const bf16x8 qtt = join_tr(lds_read_tr(qs + a1), lds_read_tr(qs + a2));
+          const int base = (32 * qb + 16 * s2) * ROW;
+          const bf16x8 dot = join_tr(lds_read_tr(Os + base + tofs[nb][0]),
+                                     lds_read_tr(Os + base + tofs[nb][1]));
+          const bf16x8 qtt = join_tr(lds_read_tr(Qs + base + tofs[nb][0]),
+                                     lds_read_tr(Qs + base + tofs[nb][1]));
           dv[nb] = mfma32(dot, pb[qb][s2], dv[nb]);
           dk[nb] = mfma32(qtt, sb[qb][s2], dk[nb]);
         }
-    }
+    wait_vmem();
     __syncthreads();
+  };
 
-    // dQ = (scale dS) K over the 128 keys: work items are (32-query block qb,
-    // 32-column slice cs); the four waves take items w, w + 4, ...
-    {
-      const size_t hb = ((size_t)b * H + h) * (size_t)Nq;
-      constexpr int NCS = D / 32;
-      for (int item = w; item < 2 * NCS; item += 4) {
-        const int qb = item / NCS;
-        const int cs = item % NCS;
-        const int ncol = 32 * cs + 16 * (li >> 4) + 4 * tr_c;
-        const int nchunk = ncol >> 3;
-        const int nsub = ncol & 7;
-        f32x16 acc = f32x16{};
-        const int icol = 32 * qb + 16 * (li >> 4) + 4 * tr_c;
-        const int ichunk = icol >> 3;
-        const int isub = icol & 7;
-#pragma unroll
-        for (int kj = 0; kj < kBK / 16; ++kj) {
-          const int r1 = 16 * kj + 4 * hh + tr_r;
-          const int r2 = r1 + 8;
-          // A = (scale dS)[i][j] (rows = queries), B = K[j][n]: both column
-          // reads of row-major LDS tiles.
-          const bf16x8 ds_op =
-              join_tr(lds_read_tr(dSt + r1 * kBQ + ((ichunk ^ tile_swz<kBQ>(r1)) * 8) + isub),
-                      lds_read_tr(dSt + r2 * kBQ + ((ichunk ^ tile_swz<kBQ>(r2)) * 8) + isub));
-          const bf16x8 k_op = join_tr(lds_read_tr(Ks + r1 * D + ((nchunk ^ tile_swz<D>(r1)) * 8) + nsub),
-                                      lds_read_tr(Ks + r2 * D + ((nchunk ^ tile_swz<D>(r2)) * 8) + nsub));
-          acc = mfma32(ds_op, k_op, acc);
-        }
-        // Lane (column 32 cs + li, hh) register r holds query row
-        // 32 qb + 8 (r/4) + 4 hh + r%4: each atomic instruction covers two
-        // contiguous 128-byte row segments.
-        float* dst = dq_acc + (hb + q0 + 32 * qb + 4 * hh) * D + 32 * cs + li;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = 8 * (r >> 2) + (r & 3);
-          if (q0 + 32 * qb + 4 * hh + qi < Nq) unsafeAtomicAdd(dst + (size_t)qi * D, acc[r]);
-        }
-      }
-    }
-
-    if (itx + 1 < n_iter) store_q(buf ^ 1);
-    __syncthreads();
+  if (n_iter > 0) load_tiles(0, sm0);
+  wait_vmem();
+  __syncthreads();
+  for (int itx = 0; itx < n_iter; itx += 2) {
+    step(itx, sm0, sm1);
+    if (itx + 1 < n_iter) step(itx + 1, sm1, sm0);
   }
 
-  // dK = scale * sum dS^T Q was folded into dS; write dK, dV for this wave's keys.
+  // Lane (key jw, hh) register r of block nb holds column 32 nb + 8 (r/4) + 4 hh + r%4.
   if (jw < Nk) {
     __bf16* dkp = dK + (((size_t)b * Hkv + g) * (size_t)Nk + jw) * D;
     __bf16* dvp = dV + (((size_t)b * Hkv + g) * (size_t)Nk + jw) * D;
@@ -368,53 +286,220 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(
   }
 }
 
-template <int D>
-size_t main_lds_bytes() {
-  return (size_t)(kBK * D + 4 * kBQ * D + kBK * kBQ) * 2 + 4 * kBQ * sizeof(float);
+// --------------------------------------------------------------------- dQ
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETA_BWD_Q_WAVES_PER_EU)))
+void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                   const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                   const float* __restrict__ LSE2, const float* __restrict__ Dsum,
+                   __bf16* __restrict__ dQ, int B, int H, int Hkv, int Nq, int Nk, float scale,
+                   float scale_log2, int n_qtiles) {
+  constexpr int NT = 256;
+  constexpr int CH = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int NB = D / 32;
+  constexpr int ROW = D * 2;
+  constexpr int TILE = kBC * ROW;
+  constexpr int NLOAD = kBC * CH / NT;
+
+  __shared__ __attribute__((aligned(16))) char sm0[2 * TILE];  // K tile | V tile
+  __shared__ __attribute__((aligned(16))) char sm1[2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31;
+  const int hh = lane >> 5;
+  const int tr_r = (lane & 15) >> 2;
+  const int tr_c = lane & 3;
+
+  const int BH = B * H;
+  const int qt = n_qtiles - 1 - blockIdx.x / BH;  // heavy query tiles first
+  const int bh = blockIdx.x % BH;
+  const int b = bh / H;
+  const int h = bh % H;
+  const int g = h / (H / Hkv);
+  const int q0 = qt * kBR;
+  const int off = Nk - Nq;
+  const int qrow = q0 + 32 * wave + li;
+  const int wave_row_lo = q0 + 32 * wave;
+
+  int n_tiles;
+  if (CAUSAL) {
+    const int last = min(Nk - 1, q0 + kBR - 1 + off);
+    n_tiles = last < 0 ? 0 : last / kBC + 1;
+  } else {
+    n_tiles = (Nk + kBC - 1) / kBC;
+  }
+
+  const size_t hq = ((size_t)b * H + h) * (size_t)Nq;
+  const buf_rsrc qrs = make_rsrc(Q + hq * D, (unsigned)Nq * ROW);
+  const buf_rsrc ors = make_rsrc(dO + hq * D, (unsigned)Nq * ROW);
+  const buf_rsrc krs = make_rsrc(K + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
+  const buf_rsrc vrs = make_rsrc(V + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
+  bf16x8 qf[KS], of[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(qrs, qrow * ROW + (16 * ks + 8 * hh) * 2, 0));
+    of[ks] = __builtin_bit_cast(bf16x8, buf_load16(ors, qrow * ROW + (16 * ks + 8 * hh) * 2, 0));
+  }
+  const float lse2 = qrow < Nq ? LSE2[hq + qrow] : 0.f;
+  const float dd = qrow < Nq ? Dsum[hq + qrow] : 0.f;
+
+  int goff[NLOAD];
+#pragma unroll
+  for (int it = 0; it < NLOAD; ++it) {
+    const int p = (wave * NLOAD + it) * 64 + lane;
+    const int row = p / CH;
+    goff[it] = row * ROW + (((p % CH) ^ tile_swz<D>(row)) * 16);
+  }
+  int kofs[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kofs[ks] = li * ROW + (((2 * ks + hh) ^ tile_swz<D>(li)) * 16);
+  int tofs[NB][2];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int rr = 4 * hh + tr_r + 8 * hf;
+      const int col = 32 * nb + 16 * (li >> 4) + 4 * tr_c;
+      tofs[nb][hf] = rr * ROW + (((col >> 3) ^ tile_swz<D>(rr)) * 16) + (col & 7) * 2;
+    }
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+
+  auto load_tile = [&](int t, char* dst) {
+    const int soff = t * TILE;
+#pragma unroll
+    for (int it = 0; it < NLOAD; ++it) {
+      char* slot = dst + (wave * NLOAD + it) * 1024;
+      buf_load16_lds(krs, slot, goff[it], soff);
+      buf_load16_lds(vrs, slot + TILE, goff[it], soff);
+    }
+  };
+
+  auto step = [&](int t, const char* Ks, char* next) {
+    const int k0 = t * kBC;
+    if (t + 1 < n_tiles) load_tile(t + 1, next);
+    const bool wave_live = !CAUSAL || (k0 <= wave_row_lo + 31 + off);
+    if (wave_live) {
+      const char* Vs = Ks + TILE;
+      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = mfma32(*(const bf16x8*)(Ks + kb * 32 * ROW + kofs[ks]), qf[ks], s[kb]);
+          dp[kb] = mfma32(*(const bf16x8*)(Vs + kb * 32 * ROW + kofs[ks]), of[ks], dp[kb]);
+        }
+      // Causal boundary, and the ragged key tail: a zero key row past Nk
+      // would contribute P * 0, but P = 2^-LSE2 can overflow for rows whose
+      // scores are all very negative, so those keys are masked to P = 0.
+      const bool need_mask = (k0 + kBC > Nk) || (CAUSAL && (k0 + kBC - 1 > wave_row_lo + off));
+      const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
+      bf16x8 sb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -lse2));
+          if (need_mask) {
+            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key > lim) p = 0.f;
+          }
+          dp[kb][r] = p * (dp[kb][r] - dd) * scale;
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = pack_bf16x2(dp[kb][8 * s2 + 2 * e], dp[kb][8 * s2 + 2 * e + 1]);
+          sb[kb][s2] = __builtin_bit_cast(bf16x8, w);
+        }
+      }
+      // dQ^T += K^T (scale dS)^T: K^T from the K tile by transpose reads.
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const char* kbase = Ks + (32 * kb + 16 * s2) * ROW;
+            const bf16x8 kt_op = join_tr(lds_read_tr(kbase + tofs[nb][0]),
+                                         lds_read_tr(kbase + tofs[nb][1]));
+            acc[nb] = mfma32(kt_op, sb[kb][s2], acc[nb]);
+          }
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  if (n_tiles > 0) load_tile(0, sm0);
+  wait_vmem();
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, sm0, sm1);
+    if (t + 1 < n_tiles) step(t + 1, sm1, sm0);
+  }
+
+  // Lane (query qrow, hh) register r of block nb holds column 32 nb + 8 (r/4) + 4 hh + r%4.
+  if (qrow < Nq) {
+    __bf16* dst = dQ + (hq + qrow) * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int n = 32 * nb + 8 * r4 + 4 * hh;
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[nb][4 * r4 + 0], acc[nb][4 * r4 + 1]);
+        w[1] = pack_bf16x2(acc[nb][4 * r4 + 2], acc[nb][4 * r4 + 3]);
+        *(u32x2*)(dst + n) = w;
+      }
+  }
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_main(const BwdArgs& a, float* dq_acc, float* dsum, hipStream_t stream) {
-  const size_t lds = main_lds_bytes<D>();
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)bwd_main_kernel<D, CAUSAL>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+hipError_t launch_main(const BwdArgs& a, const float* lse2, const float* dsum,
+                       hipStream_t stream) {
+  const float sl2 = a.scale * kLog2e;
   const int n_kt = (a.Nk + kBK - 1) / kBK;
-  dim3 grid((unsigned)(n_kt * a.B * a.Hkv));
-  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), grid, dim3(256), lds, stream,
-                     (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
-                     (const __bf16*)a.dO, a.LSE, dsum, dq_acc, (__bf16*)a.dK, (__bf16*)a.dV, a.B,
-                     a.H, a.Hkv, a.Nq, a.Nk, a.scale, a.scale * kLog2e);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(n_kt * a.B * a.Hkv)), dim3(256),
+                     0, stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
+                     (const __bf16*)a.dO, lse2, dsum, (__bf16*)a.dK, (__bf16*)a.dV, a.B, a.H,
+                     a.Hkv, a.Nq, a.Nk, a.scale, sl2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_qt = (a.Nq + kBR - 1) / kBR;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(n_qt * a.B * a.H)), dim3(256), 0,
+                     stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
+                     (const __bf16*)a.dO, lse2, dsum, (__bf16*)a.dQ, a.B, a.H, a.Hkv, a.Nq, a.Nk,
+                     a.scale, sl2, n_qt);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  float* dq_acc = (float*)a.workspace;
-  float* dsum = dq_acc + (size_t)a.B * a.H * a.Nq * D;
   const long long rows = (long long)a.B * a.H * a.Nq;
+  float* dsum = (float*)a.workspace;
+  float* lse2 = dsum + rows;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, (const __bf16*)a.O, (const __bf16*)a.dO, dsum, dq_acc, rows);
+                     stream, (const __bf16*)a.O, (const __bf16*)a.dO, a.LSE, dsum, lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = a.causal ? launch_main<D, true>(a, dq_acc, dsum, stream)
-               : launch_main<D, false>(a, dq_acc, dsum, stream);
-  if (e != hipSuccess) return e;
-  const long long n8 = rows * D / 8;
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                     dq_acc, (__bf16*)a.dQ, n8);
-  return hipGetLastError();
+  return a.causal ? launch_main<D, true>(a, lse2, dsum, stream)
+                  : launch_main<D, false>(a, lse2, dsum, stream);
 }
 
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int H, int Nq, int d) {
-  return (size_t)B * H * Nq * ((size_t)d + 1) * sizeof(float);
+  (void)d;
+  return (size_t)B * H * Nq * 2 * sizeof(float);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {

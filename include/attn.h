@@ -134,7 +134,8 @@ attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* 
                                 float scale, attn_dtype_t dtype, int chunk_tokens,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace attn_bwd needs (fp32 dQ accumulator + row term D). */
+/* Bytes of workspace attn_bwd needs: two fp32 values per query row (the row
+ * term D = rowsum(dO * O) and the base-2 log-sum-exp). */
 size_t attn_bwd_workspace_size(int B, int H, int Nq, int d);
 
 /*
@@ -147,8 +148,8 @@ size_t attn_bwd_workspace_size(int B, int H, int Nq, int d);
  *   KV gradients are summed over the query heads of each group.
  *   dtype must be BF16; d in {64, 128}.
  *   workspace: at least attn_bwd_workspace_size(B, H, Nq, d) bytes,
- *   16-byte aligned.  dQ accumulates with float atomics, so its bits may
- *   differ from run to run within rounding; dK and dV are deterministic.
+ *   16-byte aligned.  No atomics are used: dQ, dK and dV are bitwise
+ *   reproducible from run to run.
  */
 attn_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                        const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv,
