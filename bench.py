@@ -211,10 +211,10 @@ def main():
             "sum_context_tokens": sum_ctx,
             "plan": attn.attn_plan_describe(attn.ATTN_PHASE_DECODE, dw["num_seqs"], dw["Hq"],
                                             dw["Hkv"], 1, dw["ctx_hi"], dw["d"], False),
-            "roofline": {"kernel": "decode_split_kernel<128>+decode_merge_kernel", "bound": "hbm",
+            "roofline": {"kernel": "decode_split_paged_kernel<128>+decode_merge_kernel", "bound": "hbm",
                          "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                         "traffic": _traffic("decode_split_kernel<128>", dec_src, None)},
+                         "traffic": _traffic("decode_split_paged_kernel<128>", dec_src, None)},
         },
         "bwd": {
             "value": round(bwd_tflops_algo, 2),

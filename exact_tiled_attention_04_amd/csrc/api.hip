@@ -77,16 +77,18 @@ attn_status_t check_fwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, floa
 
 int plan_decode_chunk(int num_seqs, int Hkv, int max_context, int chunk_tokens) {
   if (chunk_tokens > 0) return chunk_tokens;
-  // About 128 split waves per CU if every sequence were max_context long
-  // (about half that for contexts spread uniformly below it): many short,
-  // independent K/V streams keep HBM busy, while the partials stay a few
-  // percent of the cache bytes.  Chunks are multiples of 32 tokens.
-  const long long target_units = 128LL * kNumCU;
+  // About 64 split waves per CU if every sequence were max_context long
+  // (about half that for contexts spread uniformly below it): enough
+  // independent K/V streams to keep HBM busy, each long enough to amortise
+  // its start-up, with partials a small fraction of the cache bytes.
+  // Chunks are multiples of 32 tokens (measured best: 1024 tokens for 64
+  // sequences x 8 KV heads x 32k context).
+  const long long target_units = 64LL * kNumCU;
   const long long pairs = (long long)num_seqs * Hkv;
   long long chunk = (pairs * (long long)max_context + target_units - 1) / target_units;
   chunk = (chunk + 31) / 32 * 32;
   if (chunk < 64) chunk = 64;
-  if (chunk > 4096) chunk = 4096;
+  if (chunk > 4064) chunk = 4064;
   return (int)chunk;
 }
 
@@ -105,8 +107,9 @@ attn_status_t check_decode_shape(int num_seqs, int Hq, int Hkv, int d, int block
   if ((long long)max_context > (long long)max_blocks_per_seq * block_size)
     return fail(ATTN_ERR_INVALID_ARG, "max_context=%d exceeds block table capacity %lld",
                 max_context, (long long)max_blocks_per_seq * block_size);
-  if (chunk_tokens < 0 || chunk_tokens % 32 != 0)
-    return fail(ATTN_ERR_INVALID_ARG, "chunk_tokens=%d must be 0 or a positive multiple of 32",
+  if (chunk_tokens < 0 || chunk_tokens % 32 != 0 || chunk_tokens > 4064)
+    return fail(ATTN_ERR_INVALID_ARG,
+                "chunk_tokens=%d must be 0 or a positive multiple of 32 up to 4064",
                 chunk_tokens);
   return ATTN_OK;
 }
@@ -144,7 +147,7 @@ attn_status_t attn_fwd(const void* Q, const void* K, const void* V, void* O, flo
 size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_context,
                                         int chunk_tokens) {
   if (num_seqs < 1 || Hq < 1 || (d != 64 && d != 128) || max_context < 0 || chunk_tokens < 0 ||
-      chunk_tokens % 32 != 0)
+      chunk_tokens % 32 != 0 || chunk_tokens > 4064)
     return 0;
   // The plan only needs Hkv to pick a chunk; the workspace must cover the
   // largest chunk count any Hkv could lead to, i.e. the smallest chunk.
@@ -185,6 +188,10 @@ attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* 
                 "(block=%lld token=%lld head=%lld)",
                 block_size, Hkv, d, (long long)block_stride, (long long)token_stride,
                 (long long)head_stride);
+  // The kernels address one page with 32-bit byte offsets.
+  if (block_stride >= (1LL << 30))
+    return fail(ATTN_ERR_UNSUPPORTED, "block_stride=%lld elements exceeds 2^30",
+                (long long)block_stride);
   const int chunk = plan_decode_chunk(num_seqs, Hkv, max_context, chunk_tokens);
   const int n_chunks = (max_context + chunk - 1) / chunk;
   const size_t need = eta::decode_workspace_bytes(num_seqs, Hq, d, n_chunks > 0 ? n_chunks : 1);

@@ -118,11 +118,12 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_con
  *   max_context  upper bound on context_lens (sizes the grid without reading
  *                device memory); must be <= max_blocks_per_seq*block_size.
  *   chunk_tokens context chunk per parallel work item, a positive multiple
- *                of 32, or 0 to let the library choose.
+ *                of 32 up to 4064, or 0 to let the library choose.
  *   Hq % Hkv == 0 and Hq / Hkv <= 16; d in {64, 128}; dtype must be BF16;
  *   block_size >= 1; the strides must describe non-overlapping rows:
  *   head_stride >= d, token_stride >= Hkv*head_stride,
- *   block_stride >= block_size*token_stride, all multiples of 8.
+ *   block_stride >= block_size*token_stride, all multiples of 8, and
+ *   block_stride < 2^30 (else ATTN_ERR_UNSUPPORTED).
  *   workspace    device scratch of at least
  *                attn_decode_paged_workspace_size(...) bytes, 16-byte aligned.
  */

@@ -97,6 +97,7 @@ def _decode(lib, q=FAKE, ws=FAKE, ws_bytes=1 << 30, num_seqs=2, Hq=8, Hkv=2, d=1
     (dict(d=80), attn.ATTN_ERR_UNSUPPORTED),
     (dict(max_context=65), attn.ATTN_ERR_INVALID_ARG),  # beyond 4 blocks x 16
     (dict(chunk=48), attn.ATTN_ERR_INVALID_ARG),
+    (dict(chunk=4096), attn.ATTN_ERR_INVALID_ARG),      # above the 4064-token chunk limit
     (dict(strides=(16 * 2 * 128, 128, 128)), attn.ATTN_ERR_INVALID_ARG),   # token stride < Hkv*d
     (dict(strides=(2 * 128, 2 * 128, 128)), attn.ATTN_ERR_INVALID_ARG),    # block stride too small
     (dict(strides=(16 * 2 * 132, 2 * 132, 130)), attn.ATTN_ERR_INVALID_ARG),  # unaligned head stride

@@ -51,6 +51,21 @@ def test_decode_page_and_chunk_edges(gpu, d, Hq, Hkv):
     check_lse(to64(lse), lse_ref, "bf16")
 
 
+@pytest.mark.parametrize("block_size", [1, 8, 32, 48])
+def test_block_sizes(gpu, block_size):
+    """Block sizes other than 16: multiples of 16 take the page-group path
+    (several groups per page), the others the per-token path."""
+    ctx = [1, 15, 16, 17, 47, 48, 49, 95, 96, 97, 300]
+    w = workloads.decode(num_seqs=len(ctx), Hq=16, Hkv=4, d=128, ctx_lo=0, ctx_hi=0,
+                         context_lens=ctx, block_size=block_size, dtype="bf16",
+                         seed=block_size, poison_tail=True)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = _decode(w, gpu, scale, chunk_tokens=64)
+    o_ref, lse_ref = _oracle(w, scale)
+    check_out(to64(o), o_ref, "bf16")
+    check_lse(to64(lse), lse_ref, "bf16")
+
+
 @pytest.mark.parametrize("chunk", [32, 64, 96, 256, 1024, 0])
 def test_split_count_invariance(gpu, chunk):
     """Any chunk size (any number of partials) gives the oracle's result."""
