@@ -56,6 +56,47 @@ constexpr int kMaxChunk = 4064;
 #define ETA_DECODE_WG_WAVES 4
 #endif
 
+// Work order of the split kernels.  Work item i = (sequence s, chunk c)
+// enumerates the live chunks only, sequence by sequence (c < ceil(ctx_s /
+// chunk_tokens)); a wave's slot id = i * Hkv + g.  The grid is sized for the
+// largest possible count, so the live work is dispatched first and the
+// surplus slots at the end exit at once (measured faster than a grid with
+// dead slots interleaved through it).  The wave finds its sequence by an
+// inclusive scan of the chunk counts of 64 sequences at a time.  Returns g
+// and sets s = -1 for a surplus slot.
+__device__ __forceinline__ int live_item(int slot, int Hkv, const int* __restrict__ ctx_lens,
+                                         int num_seqs, int max_context, int chunk_tokens,
+                                         int lane, int& s_out, int& chunk_out) {
+  int item = slot / Hkv;
+  const int g = slot % Hkv;
+  int s = -1, chunk = 0;
+  for (int base = 0; base < num_seqs; base += 64) {
+    const int sq = base + lane;
+    int nc = 0;
+    if (sq < num_seqs) {
+      const int c = min(ctx_lens[sq], max_context);
+      nc = c > 0 ? (c + chunk_tokens - 1) / chunk_tokens : 0;
+    }
+    int incl = nc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    const unsigned long long hit = __ballot(incl > item);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      s = base + l;
+      chunk = item - (__shfl(incl, l, 64) - __shfl(nc, l, 64));
+      break;
+    }
+    item -= __shfl(incl, 63, 64);
+  }
+  s_out = __builtin_amdgcn_readfirstlane(s);
+  chunk_out = __builtin_amdgcn_readfirstlane(chunk);
+  return g;
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * ETA_DECODE_WG_WAVES)
 __attribute__((amdgpu_waves_per_eu(ETA_DECODE_WAVES_PER_EU)))
@@ -76,11 +117,10 @@ void decode_split_paged_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * ETA_DECODE_WG_WAVES + wave;
-  const int s = blockIdx.y;
-  if (unit >= n_chunks_max * Hkv) return;
-  const int chunk = unit / Hkv;
-  const int g = unit % Hkv;
+  int s, chunk;
+  const int g = live_item(blockIdx.x * ETA_DECODE_WG_WAVES + wave, Hkv, ctx_lens, num_seqs,
+                          max_context, chunk_tokens, lane, s, chunk);
+  if (s < 0) return;
   const int ctx = min(ctx_lens[s], max_context);
   const int t_begin = chunk * chunk_tokens;
   if (t_begin >= ctx) return;
@@ -308,12 +348,11 @@ void decode_split_generic_kernel(
   __shared__ __attribute__((aligned(16))) __bf16 vs_all[4][kTok * D];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int unit = blockIdx.x * 4 + wave;
-  const int s = blockIdx.y;
-  if (unit >= n_chunks_max * Hkv) return;
-  const int chunk = unit / Hkv;
-  const int g = unit % Hkv;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int s, chunk;
+  const int g = live_item(blockIdx.x * 4 + wave, Hkv, ctx_lens, num_seqs, max_context,
+                          chunk_tokens, lane, s, chunk);
+  if (s < 0) return;
   const int ctx = min(ctx_lens[s], max_context);
   const int t_begin = chunk * chunk_tokens;
   if (t_begin >= ctx) return;
@@ -504,18 +543,38 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
   const int n = threadIdx.x;
   const int ctx = min(ctx_lens[s], max_context);
   const int nc = ctx > 0 ? (ctx + chunk_tokens - 1) / chunk_tokens : 0;
-  float big_m = -INFINITY;
-  for (int c = 0; c < nc; ++c) {
-    const size_t row = ((size_t)c * num_seqs + s) * Hq + hq;
-    big_m = fmaxf(big_m, part_ml[row * 2]);
-  }
-  const float m_use = big_m == -INFINITY ? 0.f : big_m;
-  float acc = 0.f, ell = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const size_t row = ((size_t)c * num_seqs + s) * Hq + hq;
-    const float w = fast_exp2(part_ml[row * 2] - m_use);
-    ell += w * part_ml[row * 2 + 1];
-    acc += w * part_o[row * D + n];
+  // One pass over the chunks, kBatch at a time: all loads of a batch are
+  // issued before any is used (the partials are latency-bound, not
+  // bandwidth-bound), then the running max absorbs the batch's max and the
+  // sums are rescaled by 2^(old - new), as in the online softmax.
+  constexpr int kBatch = 8;
+  const size_t stride = (size_t)num_seqs * Hq;
+  const size_t row0 = (size_t)s * Hq + hq;
+  float big_m = -INFINITY, acc = 0.f, ell = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += kBatch) {
+    float mv[kBatch], lv[kBatch], ov[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool ok = c0 + j < nc;
+      const size_t row = (size_t)(ok ? c0 + j : 0) * stride + row0;
+      mv[j] = ok ? part_ml[row * 2] : -INFINITY;
+      lv[j] = ok ? part_ml[row * 2 + 1] : 0.f;
+      ov[j] = ok ? part_o[row * D + n] : 0.f;
+    }
+    float bm = big_m;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) bm = fmaxf(bm, mv[j]);
+    if (bm == -INFINITY) continue;  // every chunk so far saw no key
+    const float r = fast_exp2(big_m - bm);  // 0 while big_m is -inf
+    acc *= r;
+    ell *= r;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float w = fast_exp2(mv[j] - bm);
+      ell += w * lv[j];
+      acc += w * ov[j];
+    }
+    big_m = bm;
   }
   const float inv = ell > 0.f ? 1.f / ell : 0.f;
   const size_t orow = (size_t)s * Hq + hq;
@@ -531,7 +590,10 @@ hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t
     const int units = p.n_chunks_max * a.Hkv;
     const bool paged = a.block_size % 16 == 0;
     const int wg_waves = paged ? ETA_DECODE_WG_WAVES : 4;
-    dim3 grid((unsigned)((units + wg_waves - 1) / wg_waves), (unsigned)a.num_seqs);
+    // Every (sequence, chunk, KV head) slot the grid could need; the slots
+    // beyond the live work exit at once (and come last in launch order).
+    const long long slots = (long long)units * a.num_seqs;
+    dim3 grid((unsigned)((slots + wg_waves - 1) / wg_waves));
     auto kern = paged ? decode_split_paged_kernel<D> : decode_split_generic_kernel<D>;
     hipLaunchKernelGGL(kern, grid, dim3(64 * wg_waves), 0, stream,
                        (const __bf16*)a.Q, (const __bf16*)a.K_cache, (const __bf16*)a.V_cache,

@@ -78,6 +78,27 @@ def test_split_count_invariance(gpu, chunk):
     check_lse(to64(lse), lse_ref, "bf16")
 
 
+@pytest.mark.parametrize("block_size", [16, 8])
+def test_many_sequences_with_empty_ones(gpu, block_size):
+    """More than 64 sequences (the split kernels locate their sequence 64 at
+    a time), many of them empty, so the live work items are packed across
+    sequence-group boundaries."""
+    rng = np.random.default_rng(31)
+    ctx = rng.integers(1, 200, size=150)
+    ctx[rng.random(150) < 0.3] = 0
+    ctx[[0, 63, 64, 127, 128, 149]] = [0, 199, 0, 1, 64, 33]
+    w = workloads.decode(num_seqs=150, Hq=8, Hkv=2, d=128, ctx_lo=0, ctx_hi=0,
+                         context_lens=ctx.tolist(), block_size=block_size, dtype="bf16",
+                         seed=31, poison_tail=True)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = _decode(w, gpu, scale, chunk_tokens=32)
+    o_ref, lse_ref = _oracle(w, scale)
+    empty = torch.from_numpy(ctx == 0)
+    assert torch.all(o[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
+    check_out(to64(o), o_ref, "bf16")
+    check_lse(to64(lse), lse_ref, "bf16")
+
+
 def test_empty_and_clamped_contexts(gpu):
     """ctx <= 0 gives O = 0, LSE = -inf; ctx above max_context is clamped."""
     w = workloads.decode(num_seqs=4, Hq=8, Hkv=2, d=128, ctx_lo=0, ctx_hi=0,
