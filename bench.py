@@ -192,13 +192,13 @@ def main():
                                             fw["Nq"], fw["Nk"], fw["d"], True),
         },
         "roofline": {
-            "kernel": "fwd_bf16_kernel<128,causal,4>",
+            "kernel": "fwd_bf16_kernel<128,causal,4,32>",
             "bound": "mfma",
             "achieved": round(fwd_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": _traffic("fwd_bf16_kernel<128,causal,4>", fwd_src, None),
+            "traffic": _traffic("fwd_bf16_kernel<128,causal,4,32>", fwd_src, None),
             "avg_launch_ms": round(fwd_avg, 4),
             "algorithmic_flop_per_launch": fwd_flops,
         },

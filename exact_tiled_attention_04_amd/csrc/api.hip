@@ -34,12 +34,14 @@ attn_status_t ok() {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int kNumCU = 256;        // MI355X compute units
+
 constexpr long long kMaxGrid = 0x7fffffffLL;
 
 // ---------------------------------------------------------------- forward
 
-eta::FwdPlan plan_fwd(int B, int H, int Nq, bool bf16) {
+eta::FwdPlan plan_fwd(int B, int H, int Nq, int d, bool bf16) {
   eta::FwdPlan p;
+  p.rows_per_wave = 32;
   if (bf16) {
     // One wave = 32 query rows.  Four waves per workgroup share each K/V
     // tile; when that leaves fewer than two workgroups per CU, halve the
@@ -47,12 +49,12 @@ eta::FwdPlan plan_fwd(int B, int H, int Nq, bool bf16) {
     p.waves = 4;
     long long wgs = (long long)B * H * ((Nq + 127) / 128);
     if (wgs < 2LL * kNumCU) p.waves = 2;
-    p.block_keys = 64;
+    p.block_keys = d == 128 ? 32 : 64;
   } else {
     p.waves = 4;
     p.block_keys = 32;
   }
-  p.block_rows = 32 * p.waves;
+  p.block_rows = p.rows_per_wave * p.waves;
   p.workgroups = (long long)B * H * ((Nq + p.block_rows - 1) / p.block_rows);
   return p;
 }
@@ -137,7 +139,7 @@ attn_status_t attn_fwd(const void* Q, const void* K, const void* V, void* O, flo
   attn_status_t st = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale, dtype);
   if (st != ATTN_OK) return st;
   eta::FwdArgs a{Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, causal, dtype == ATTN_DTYPE_BF16};
-  eta::FwdPlan p = plan_fwd(B, H, Nq, a.dtype_bf16);
+  eta::FwdPlan p = plan_fwd(B, H, Nq, d, a.dtype_bf16);
   if (p.workgroups > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "grid too large");
   hipError_t e = eta::launch_fwd(a, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
@@ -244,13 +246,14 @@ int attn_plan_describe(int phase, int B, int H, int Hkv, int Nq, int Nk, int d, 
   if (phase == ATTN_PHASE_FWD) {
     if (check_fwd_shape(B, H, Hkv, Nq, Nk, d, 1.f, dtype) != ATTN_OK) return -1;
     const bool bf16 = dtype == ATTN_DTYPE_BF16;
-    eta::FwdPlan p = plan_fwd(B, H, Nq, bf16);
+    eta::FwdPlan p = plan_fwd(B, H, Nq, d, bf16);
     n = snprintf(tmp, sizeof(tmp),
-                 "phase=fwd kernel=%s d=%d causal=%d Br=%d (%d waves x 32 rows) Bc=%d "
+                 "phase=fwd kernel=%s d=%d causal=%d Br=%d (%d waves x %d rows) Bc=%d "
                  "grid=%lld workgroups (B*H*ceil(Nq/Br)) order=heavy-query-tiles-first "
                  "head-interleaved",
-                 bf16 ? "fwd_bf16_mfma32x32x16" : "fwd_f32_mfma32x32x2", d, causal ? 1 : 0,
-                 p.block_rows, p.waves, p.block_keys, p.workgroups);
+                 bf16 ? "fwd_bf16_mfma32x32x16" : "fwd_f32_mfma32x32x2",
+                 d, causal ? 1 : 0, p.block_rows, p.waves, p.rows_per_wave, p.block_keys,
+                 p.workgroups);
   } else if (phase == ATTN_PHASE_DECODE) {
     if (check_decode_shape(B, H, Hkv, d, 16, 1, (Nk + 15) / 16 > 0 ? (Nk + 15) / 16 : 1, Nk, 0) !=
         ATTN_OK)

@@ -34,12 +34,14 @@ namespace eta {
 
 namespace {
 
-constexpr int kBC = 64;  // keys per K/V tile
 
-// Two waves per SIMD: the softmax of one wave overlaps the MFMAs of the other.
-#ifndef ETA_FWD_WAVES_PER_EU
-#define ETA_FWD_WAVES_PER_EU 2
-#endif
+// Key-tile width per head dimension: 32 keys for d = 128 (32 KiB of LDS
+// and 154 VGPRs, so three waves share each SIMD: measured 4% faster than
+// 64-key tiles at two waves per SIMD), 64 keys for d = 64 (fewer barriers;
+// measured 3% faster than 32).  More waves per SIMD let one wave's softmax
+// overlap another's MFMAs.
+template <int D>
+constexpr int fwd_bc() { return D == 128 ? 32 : 64; }
 
 // The running maximum is a reference point, not necessarily the exact row
 // maximum: it moves (and the accumulator is rescaled) only when a tile's
@@ -49,8 +51,8 @@ constexpr int kBC = 64;  // keys per K/V tile
 constexpr float kSlack = 8.f;
 
 
-template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(ETA_FWD_WAVES_PER_EU)))
+template <int D, bool CAUSAL, int NW, int BC>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BC == 32 ? 3 : 2)))
 void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
@@ -58,12 +60,14 @@ void fwd_bf16_kernel(
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;
   constexpr int CH = D / 8;                  // 16-byte chunks per row
-  constexpr int NLOAD = kBC * CH / NT;       // 16-byte loads per thread per tile
+  constexpr int NLOAD = BC * CH / NT;       // 16-byte loads per thread per tile
   constexpr int KS = D / 16;                 // k-steps of the QK^T product
   constexpr int NB = D / 32;                 // 32-wide column blocks of o
   constexpr int ROW = D * 2;                 // bytes per row
-  constexpr int TILE = kBC * ROW;            // bytes per K (or V) tile
-  static_assert(kBC * CH % NT == 0, "tile load split");
+  constexpr int TILE = BC * ROW;            // bytes per K (or V) tile
+  constexpr int KB = BC / 32;                // 32-key blocks per tile
+  static_assert(BC * CH % NT == 0, "tile load split");
+  static_assert(BC == 32 || BC == 64, "tile width");
 
   // Two LDS buffers (K tile then V tile each) as separate objects, so the
   // direct copies into one are known not to alias reads of the other.
@@ -101,9 +105,9 @@ void fwd_bf16_kernel(
   int n_tiles;
   if (CAUSAL) {
     int last = min(Nk - 1, q0 + BR - 1 + off);
-    n_tiles = last < 0 ? 0 : last / kBC + 1;
+    n_tiles = last < 0 ? 0 : last / BC + 1;
   } else {
-    n_tiles = (Nk + kBC - 1) / kBC;
+    n_tiles = (Nk + BC - 1) / BC;
   }
 
   // Queries of this lane's row as the B operand (Q^T); rows past Nq read 0.
@@ -153,36 +157,40 @@ void fwd_bf16_kernel(
   };
 
   auto step = [&](int t, const char* Ks, char* next) {
-    const int k0 = t * kBC;
+    const int k0 = t * BC;
     if (t + 1 < n_tiles) load_tile(t + 1, next);
     // Tiles wholly above this wave's diagonal contribute nothing.
     const bool wave_live = !CAUSAL || (k0 <= wave_row_lo + 31 + off);
     if (wave_live) {
       const char* Vs = Ks + TILE;
-      // S^T for keys 0..31 (s[0]) and 32..63 (s[1]); the two accumulation
-      // chains interleave and each k-step's K operands are read one step ahead.
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-      bf16x8 a0 = *(const bf16x8*)(Ks + kofs[0]);
-      bf16x8 a1 = *(const bf16x8*)(Ks + 32 * ROW + kofs[0]);
+      // S^T for keys 32 kb .. 32 kb + 31 (s[kb]); with two blocks the
+      // accumulation chains interleave; each k-step's K operands are read one
+      // step ahead.
+      f32x16 s[KB];
+      bf16x8 a[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        s[kb] = f32x16{};
+        a[kb] = *(const bf16x8*)(Ks + 32 * kb * ROW + kofs[0]);
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 n0 = a0, n1 = a1;
-        if (ks + 1 < KS) {
-          n0 = *(const bf16x8*)(Ks + kofs[ks + 1]);
-          n1 = *(const bf16x8*)(Ks + 32 * ROW + kofs[ks + 1]);
-        }
-        s[0] = mfma32(a0, qf[ks], s[0]);
-        s[1] = mfma32(a1, qf[ks], s[1]);
-        a0 = n0;
-        a1 = n1;
+        bf16x8 n[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          n[kb] = (ks + 1 < KS) ? *(const bf16x8*)(Ks + 32 * kb * ROW + kofs[ks + 1]) : a[kb];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) s[kb] = mfma32(a[kb], qf[ks], s[kb]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) a[kb] = n[kb];
       }
 
       // Mask the causal boundary and the ragged key tail.
-      const bool need_mask = (k0 + kBC > Nk) || (CAUSAL && (k0 + kBC - 1 > wave_row_lo + off));
+      const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wave_row_lo + off));
       if (need_mask) {
         const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -195,7 +203,9 @@ void fwd_bf16_kernel(
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+      for (int kb = 1; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       const float mx2 = halves_max(mx) * scale_log2;
       if (wave_any(mx2 > m_run + kSlack)) {
         const float m_new = fmaxf(m_run, mx2);
@@ -210,7 +220,7 @@ void fwd_bf16_kernel(
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
@@ -220,9 +230,9 @@ void fwd_bf16_kernel(
       l_run += rs;
 
       // P (bf16) as the B operand of o^T += V^T P^T, 16 keys per MFMA.
-      bf16x8 pb[2][2];
+      bf16x8 pb[KB][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           u32x4 w;
@@ -232,16 +242,17 @@ void fwd_bf16_kernel(
         }
       // o^T += V^T P^T: 4 MFMAs per 32-column block, V^T operands read one
       // MFMA ahead.
+      constexpr int PV = 2 * KB;  // 16-key MFMA steps per tile
       auto vread = [&](int i) {
-        const int nb = i >> 2, kb = (i >> 1) & 1, s2 = i & 1;
+        const int nb = i / PV, kb = (i % PV) >> 1, s2 = i & 1;
         const char* vb = Vs + (32 * kb + 16 * s2) * ROW;
         return join_tr(lds_read_tr(vb + vofs[nb][0]), lds_read_tr(vb + vofs[nb][1]));
       };
       bf16x8 va = vread(0);
 #pragma unroll
-      for (int i = 0; i < 4 * NB; ++i) {
-        const bf16x8 vn = (i + 1 < 4 * NB) ? vread(i + 1) : va;
-        o[i >> 2] = mfma32(va, pb[(i >> 1) & 1][i & 1], o[i >> 2]);
+      for (int i = 0; i < PV * NB; ++i) {
+        const bf16x8 vn = (i + 1 < PV * NB) ? vread(i + 1) : va;
+        o[i / PV] = mfma32(va, pb[(i % PV) >> 1][i & 1], o[i / PV]);
         va = vn;
       }
     }
@@ -427,19 +438,21 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_bf16(const FwdArgs& a, int nw, hipStream_t stream) {
-  const int br = nw * 32;
+hipError_t launch_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
+  const int br = p.block_rows;
   const int n_qtiles = (a.Nq + br - 1) / br;
   dim3 grid((unsigned)(n_qtiles * a.B * a.H));
   const float sl2 = a.scale * kLog2e;
-  if (nw == 4) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), grid, dim3(256), 0, stream,
-                       (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
-                       a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles);
+  const __bf16* q = (const __bf16*)a.Q;
+  const __bf16* k = (const __bf16*)a.K;
+  const __bf16* v = (const __bf16*)a.V;
+  __bf16* o = (__bf16*)a.O;
+  if (p.waves == 4) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, fwd_bc<D>()>), grid, dim3(256), 0, stream, q, k,
+                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles);
   } else {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 2>), grid, dim3(128), 0, stream,
-                       (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V, (__bf16*)a.O,
-                       a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 2, fwd_bc<D>()>), grid, dim3(128), 0, stream, q, k,
+                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles);
   }
   return hipGetLastError();
 }
@@ -460,10 +473,9 @@ hipError_t launch_f32(const FwdArgs& a, hipStream_t stream) {
 hipError_t launch_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
   if (a.dtype_bf16) {
     if (a.d == 128)
-      return a.causal ? launch_bf16<128, true>(a, p.waves, stream)
-                      : launch_bf16<128, false>(a, p.waves, stream);
-    return a.causal ? launch_bf16<64, true>(a, p.waves, stream)
-                    : launch_bf16<64, false>(a, p.waves, stream);
+      return a.causal ? launch_bf16<128, true>(a, p, stream)
+                      : launch_bf16<128, false>(a, p, stream);
+    return a.causal ? launch_bf16<64, true>(a, p, stream) : launch_bf16<64, false>(a, p, stream);
   }
   if (a.d == 128)
     return a.causal ? launch_f32<128, true>(a, stream) : launch_f32<128, false>(a, stream);

@@ -20,7 +20,8 @@ struct FwdArgs {
 };
 
 struct FwdPlan {
-  int waves;        // waves per workgroup (32 query rows each)
+  int waves;        // waves per workgroup
+  int rows_per_wave;  // query rows per wave
   int block_rows;   // query rows per workgroup
   int block_keys;   // keys per K/V tile
   long long workgroups;
