@@ -27,17 +27,31 @@ import math
 import numpy as np
 
 
-def _visible(nq, nk, causal):
+def _visible(nq, nk, causal, window=None):
     """Boolean [nq, nk] visibility of key j from query row i.
 
     [MAK] "Kernel structure": causal attention hides every key after the
     query's own position; bottom-right aligned as stated in the module notes.
+    The same section says local attention changes the range of keys a query
+    visits, and [AK]'s sparse-attention paragraph names the sliding window
+    (each position sees a fixed number of recent positions).  ``window`` =
+    (left, right) keeps key j only if p - left <= j <= p + right, where p is
+    the row's bottom-right aligned position; either side may be None
+    (unbounded).  A sliding window of W keys is (W - 1, 0).  The window and the
+    causal mask combine by intersection.
     """
-    if not causal:
-        return np.ones((nq, nk), dtype=bool)
     row_pos = np.arange(nq)[:, None] + (nk - nq)
     col = np.arange(nk)[None, :]
-    return col <= row_pos
+    vis = np.ones((nq, nk), dtype=bool)
+    if causal:
+        vis &= col <= row_pos
+    if window is not None:
+        left, right = window
+        if left is not None:
+            vis &= col >= row_pos - left
+        if right is not None:
+            vis &= col <= row_pos + right
+    return vis
 
 
 def _check_shapes(q, k, v):
@@ -52,7 +66,7 @@ def _check_shapes(q, k, v):
     return h // hkv
 
 
-def forward_probs(q, k, v, scale, causal):
+def forward_probs(q, k, v, scale, causal, window=None):
     """Materialised attention: returns (O, LSE, P).
 
     [MAK] "Standard attention materializes quadratic state":
@@ -64,6 +78,7 @@ def forward_probs(q, k, v, scale, causal):
     row; one natural-log number carries both).
 
     q: [B, H, Nq, d]; k, v: [B, Hkv, Nk, d] (any float dtype, computed in fp64).
+    window: optional (left, right) local-attention band, see ``_visible``.
     Returns O [B, H, Nq, d], LSE [B, H, Nq], P [B, H, Nq, Nk], all float64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -72,7 +87,7 @@ def forward_probs(q, k, v, scale, causal):
     group = _check_shapes(q, k, v)
     bsz, nh, nq, d = q.shape
     nk = k.shape[2]
-    vis = _visible(nq, nk, causal)
+    vis = _visible(nq, nk, causal, window)
 
     out = np.zeros((bsz, nh, nq, d))
     lse = np.full((bsz, nh, nq), -np.inf)
@@ -95,13 +110,13 @@ def forward_probs(q, k, v, scale, causal):
     return out, lse, probs
 
 
-def forward(q, k, v, scale, causal):
+def forward(q, k, v, scale, causal, window=None):
     """(O, LSE) of :func:`forward_probs`."""
-    out, lse, _ = forward_probs(q, k, v, scale, causal)
+    out, lse, _ = forward_probs(q, k, v, scale, causal, window)
     return out, lse
 
 
-def backward(q, k, v, do, scale, causal):
+def backward(q, k, v, do, scale, causal, window=None):
     """Gradients of L = sum(O * dO) with respect to Q, K, V.
 
     [MAK] "Backward pass recomputes scores" and [FIO]'s backward paragraph
@@ -127,7 +142,7 @@ def backward(q, k, v, do, scale, causal):
     group = _check_shapes(q, k, v)
     if do.shape != q.shape:
         raise ValueError("dO must have Q's shape")
-    _, _, p_all = forward_probs(q, k, v, scale, causal)
+    _, _, p_all = forward_probs(q, k, v, scale, causal, window)
     bsz, nh, _, _ = q.shape
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -195,13 +210,15 @@ def decode_paged(q, k_cache, v_cache, block_table, context_lens, scale):
     return out, lse
 
 
-def brute_force_forward(q, k, v, scale, causal):
+def brute_force_forward(q, k, v, scale, causal, window=None):
     """Scalar pure-Python attention for tiny inputs (N <= 8, d <= 8).
 
     A second evaluation of the same definition with no numpy arithmetic:
-    nested loops, math.exp, and a max taken over the visible keys only.
+    nested loops, math.exp, and a max taken over the visible keys only (the
+    visibility test written out again, not shared with ``_visible``).
     Inputs are nested lists or arrays; returns nested lists O, LSE.
     """
+    left, right = window if window is not None else (None, None)
     q = np.asarray(q, dtype=np.float64).tolist()
     k = np.asarray(k, dtype=np.float64).tolist()
     v = np.asarray(v, dtype=np.float64).tolist()
@@ -217,7 +234,12 @@ def brute_force_forward(q, k, v, scale, causal):
             for i in range(nq):
                 scores = []
                 for j in range(nk):
-                    if causal and j > i + (nk - nq):
+                    pos = i + (nk - nq)
+                    if causal and j > pos:
+                        continue
+                    if left is not None and j < pos - left:
+                        continue
+                    if right is not None and j > pos + right:
                         continue
                     dot = 0.0
                     for c in range(d):

@@ -461,7 +461,7 @@ def test_planted_mask_off_by_one_is_caught(monkeypatch):
     assert _pins_pass()
     real = oatt._visible
     monkeypatch.setattr(oatt, "_visible",
-                        lambda nq, nk, c: real(nq, nk + 1, c)[:, :nk] if c else real(nq, nk, c))
+                        lambda nq, nk, c, w=None: real(nq, nk + 1, c, w)[:, :nk] if c else real(nq, nk, c, w))
     assert not _pins_pass()
 
 
@@ -478,7 +478,7 @@ def test_planted_group_map_is_caught(monkeypatch):
 
 def test_planted_dropped_scale_is_caught(monkeypatch):
     real = oatt.forward_probs
-    monkeypatch.setattr(oatt, "forward_probs", lambda q, k, v, s, c: real(q, k, v, 1.0, c))
+    monkeypatch.setattr(oatt, "forward_probs", lambda q, k, v, s, c, w=None: real(q, k, v, 1.0, c, w))
     assert not _pins_pass()
 
 
@@ -490,8 +490,8 @@ def test_planted_backward_sign_is_caught(monkeypatch):
     do = _rand((1, 1, 4, 3), 56)
     real_fp = oatt.forward_probs
 
-    def neg_p(q_, k_, v_, s_, c_):
-        o_, l_, p_ = real_fp(q_, k_, v_, s_, c_)
+    def neg_p(q_, k_, v_, s_, c_, w_=None):
+        o_, l_, p_ = real_fp(q_, k_, v_, s_, c_, w_)
         return o_, l_, p_.transpose(0, 1, 3, 2)  # transposed P
     monkeypatch.setattr(oatt, "forward_probs", neg_p)
     dq, dk, dv = oatt.backward(q, k, v, do, 0.5, False)
@@ -503,3 +503,131 @@ def test_planted_backward_sign_is_caught(monkeypatch):
         vm = v.copy(); vm[idx] -= eps
         num[idx] = (_loss(q, k, vp, do, 0.5, False) - _loss(q, k, vm, do, 0.5, False)) / (2 * eps)
     assert not np.allclose(dv, num, rtol=1e-6, atol=1e-8)
+
+
+# ------------------------------------------------------- local (window) band
+
+WINDOWS = [
+    # Nq, Nk, causal, (left, right)
+    (6, 6, True, (2, None)),      # sliding window of 3 keys
+    (6, 6, False, (1, 1)),        # symmetric band
+    (5, 8, True, (3, None)),      # rectangular, bottom-right aligned
+    (7, 4, False, (0, 2)),        # Nq > Nk: early rows see few or no keys
+    (6, 6, False, (None, 0)),     # right = 0 alone is the causal mask
+    (6, 6, False, (0, 0)),        # the diagonal only
+]
+
+
+@pytest.mark.parametrize("Nq,Nk,causal,window", WINDOWS)
+def test_window_brute_force_agrees(Nq, Nk, causal, window):
+    q = _rand((1, 2, Nq, 4), 60)
+    k = _rand((1, 1, Nk, 4), 61)
+    v = _rand((1, 1, Nk, 4), 62)
+    o, lse = oracle.forward(q, k, v, 0.5, causal, window)
+    ob, lb = oracle.brute_force_forward(q, k, v, 0.5, causal, window)
+    np.testing.assert_allclose(o, np.array(ob), rtol=0, atol=1e-12)
+    lb = np.array(lb)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lb))
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(lse[fin], lb[fin], rtol=0, atol=1e-12)
+
+
+def test_window_special_cases():
+    """A window wider than the sequence is the plain mask; right = 0 is the
+    causal mask; (0, 0) picks exactly the diagonal key: O_i = V_p and
+    LSE_i = s_ip."""
+    q = _rand((1, 1, 7, 5), 63)
+    k = _rand((1, 1, 7, 5), 64)
+    v = _rand((1, 1, 7, 5), 65)
+    ref_c, lse_c = oracle.forward(q, k, v, 0.7, True)
+    for w in [(7, None), (100, 0), (None, None)]:
+        o, lse = oracle.forward(q, k, v, 0.7, True, w)
+        np.testing.assert_array_equal(o, ref_c)
+        np.testing.assert_array_equal(lse, lse_c)
+    o, lse = oracle.forward(q, k, v, 0.7, False, (None, 0))
+    np.testing.assert_array_equal(o, ref_c)
+    ref_f, _ = oracle.forward(q, k, v, 0.7, False)
+    o, _ = oracle.forward(q, k, v, 0.7, False, (50, 50))
+    np.testing.assert_array_equal(o, ref_f)
+    o, lse = oracle.forward(q, k, v, 0.7, False, (0, 0))
+    np.testing.assert_allclose(o[0, 0], v[0, 0], atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0], 0.7 * (q[0, 0] * k[0, 0]).sum(-1), atol=1e-14)
+
+
+@pytest.mark.parametrize("Nq,Nk,window", [(9, 9, (3, 0)), (6, 10, (2, 1)), (8, 5, (1, 3))])
+def test_window_q_zero_closed_form(Nq, Nk, window):
+    """Q = 0: O_i is the mean of V over the keys max(0, p - left) ..
+    min(Nk - 1, p + right), LSE_i = ln(count); an empty range gives 0, -inf."""
+    left, right = window
+    q = np.zeros((1, 1, Nq, 3))
+    k = _rand((1, 1, Nk, 3), 66)
+    v = _rand((1, 1, Nk, 3), 67)
+    o, lse = oracle.forward(q, k, v, 0.9, False, window)
+    for i in range(Nq):
+        p = i + Nk - Nq
+        lo, hi = max(0, p - left), min(Nk - 1, p + right)
+        if lo > hi:
+            assert np.all(o[0, 0, i] == 0) and np.isneginf(lse[0, 0, i])
+            continue
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, lo:hi + 1].mean(0), atol=1e-14)
+        np.testing.assert_allclose(lse[0, 0, i], math.log(hi - lo + 1), atol=1e-14)
+
+
+def test_window_torch_sdpa_band_mask():
+    """torch's fp64 attention with the band written as a boolean mask."""
+    B, H, Hkv, Nq, Nk, d = 1, 4, 2, 12, 16, 8
+    left, right = 4, 1
+    q = _rand((B, H, Nq, d), 68)
+    k = _rand((B, Hkv, Nk, d), 69)
+    v = _rand((B, Hkv, Nk, d), 70)
+    o, _ = oracle.forward(q, k, v, 0.35, False, (left, right))
+    i = torch.arange(Nq)[:, None] + (Nk - Nq)
+    j = torch.arange(Nk)[None, :]
+    band = (j >= i - left) & (j <= i + right)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=band,
+        scale=0.35, enable_gqa=True).numpy()
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,window", [(True, (2, None)), (False, (1, 2))])
+def test_window_backward_finite_differences(causal, window):
+    q = _rand((1, 2, 5, 3), 71)
+    k = _rand((1, 1, 6, 3), 72)
+    v = _rand((1, 1, 6, 3), 73)
+    do = _rand((1, 2, 5, 3), 74)
+    scale = 0.8
+    grads = oracle.backward(q, k, v, do, scale, causal, window)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.forward(q_, k_, v_, scale, causal, window)
+        return float((o * do).sum())
+    eps = 1e-6
+    for which, (x, g) in enumerate(zip((q, k, v), grads)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            a_p = [q, k, v]; a_p[which] = xp
+            a_m = [q, k, v]; a_m[which] = xm
+            num[idx] = (loss(*a_p) - loss(*a_m)) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_planted_window_off_by_one_is_caught(monkeypatch):
+    """A window that keeps one key too many on the left fails the brute force."""
+    q = _rand((1, 1, 6, 4), 75)
+    k = _rand((1, 1, 6, 4), 76)
+    v = _rand((1, 1, 6, 4), 77)
+    real = oatt._visible
+
+    def wrong(nq, nk, c, w=None):
+        if w is None:
+            return real(nq, nk, c, w)
+        return real(nq, nk, c, (w[0] + 1 if w[0] is not None else None, w[1]))
+    monkeypatch.setattr(oatt, "_visible", wrong)
+    o, _ = oracle.forward(q, k, v, 0.5, True, (2, None))
+    ob, _ = oracle.brute_force_forward(q, k, v, 0.5, True, (2, None))
+    assert not np.allclose(o, np.array(ob), atol=1e-6)
