@@ -7,9 +7,9 @@ in the library's HIP kernels.  There is no fallback: if the library has not
 been built (``python -m exact_tiled_attention_04_amd.build``) the first call
 raises.
 
-Names follow the C ABI: ``attn_fwd``, ``attn_decode_paged``, ``attn_bwd``,
-``attn_decode_paged_workspace_size``, ``attn_bwd_workspace_size``,
-``attn_plan_describe``, ``attn_status_string``.
+Names follow the C ABI: ``attn_fwd``, ``attn_fwd_local``, ``attn_decode_paged``,
+``attn_bwd``, ``attn_bwd_local``, ``attn_decode_paged_workspace_size``,
+``attn_bwd_workspace_size``, ``attn_plan_describe``, ``attn_status_string``.
 """
 
 import ctypes
@@ -34,6 +34,8 @@ ATTN_PHASE_BWD = 2
 
 EXPORTED = (
     "attn_fwd",
+    "attn_fwd_local",
+    "attn_bwd_local",
     "attn_decode_paged_workspace_size",
     "attn_decode_paged",
     "attn_bwd_workspace_size",
@@ -68,6 +70,9 @@ def load_library(path=LIB_PATH):
                              ctypes.c_size_t)
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
     lib.attn_fwd.restype = i32
+    lib.attn_fwd_local.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
+                                   i32, vp]
+    lib.attn_fwd_local.restype = i32
     lib.attn_decode_paged_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_decode_paged_workspace_size.restype = sz
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -78,6 +83,9 @@ def load_library(path=LIB_PATH):
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                              f32, i32, i32, vp, sz, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_local.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                   i32, f32, i32, i32, i32, vp, sz, vp]
+    lib.attn_bwd_local.restype = i32
     lib.attn_plan_describe.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                        ctypes.c_char_p, sz]
     lib.attn_plan_describe.restype = i32
@@ -127,9 +135,7 @@ def _need_device(*ts):
             raise ValueError("tensors must be contiguous")
 
 
-def attn_fwd(q, k, v, scale, causal, out=None, lse=None, stream=None):
-    """O, LSE = attention(q, k, v).  q [B,H,Nq,d]; k, v [B,Hkv,Nk,d]."""
-    lib = load_library()
+def _fwd_args(q, k, v, out, lse):
     _need_device(q, k, v)
     B, H, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
@@ -142,8 +148,26 @@ def attn_fwd(q, k, v, scale, causal, out=None, lse=None, stream=None):
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     _need_device(out, lse)
-    _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Nq, Nk, d,
-                        float(scale), int(bool(causal)), _dtype_code(q), _stream(stream)))
+    return (B, H, Hkv, Nq, Nk, d), out, lse
+
+
+def attn_fwd(q, k, v, scale, causal, out=None, lse=None, stream=None):
+    """O, LSE = attention(q, k, v).  q [B,H,Nq,d]; k, v [B,Hkv,Nk,d]."""
+    lib = load_library()
+    dims, out, lse = _fwd_args(q, k, v, out, lse)
+    _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *dims, float(scale),
+                        int(bool(causal)), _dtype_code(q), _stream(stream)))
+    return out, lse
+
+
+def attn_fwd_local(q, k, v, scale, window_left, window_right, out=None, lse=None, stream=None):
+    """attn_fwd with the band p - window_left <= j <= p + window_right (-1: no
+    limit on that side); (W - 1, 0) is a sliding window of W keys."""
+    lib = load_library()
+    dims, out, lse = _fwd_args(q, k, v, out, lse)
+    _check(lib.attn_fwd_local(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *dims,
+                              float(scale), int(window_left), int(window_right), _dtype_code(q),
+                              _stream(stream)))
     return out, lse
 
 
@@ -191,10 +215,7 @@ def attn_bwd_workspace_size(B, H, Nq, d):
     return int(load_library().attn_bwd_workspace_size(B, H, Nq, d))
 
 
-def attn_bwd(q, k, v, o, do, lse, scale, causal, dq=None, dk=None, dv=None, workspace=None,
-             stream=None):
-    """dQ, dK, dV of attention given the forward's O and LSE."""
-    lib = load_library()
+def _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace):
     _need_device(q, k, v, o, do, lse)
     B, H, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
@@ -204,10 +225,29 @@ def attn_bwd(q, k, v, o, do, lse, scale, causal, dq=None, dk=None, dv=None, work
     need = attn_bwd_workspace_size(B, H, Nq, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    return (B, H, Hkv, Nq, Nk, d), dq, dk, dv, workspace
+
+
+def attn_bwd(q, k, v, o, do, lse, scale, causal, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
+    """dQ, dK, dV of attention given the forward's O and LSE."""
+    lib = load_library()
+    dims, dq, dk, dv, workspace = _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace)
     _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
-                        _ptr(dk), _ptr(dv), B, H, Hkv, Nq, Nk, d, float(scale),
-                        int(bool(causal)), _dtype_code(q), _ptr(workspace), workspace.numel(),
-                        _stream(stream)))
+                        _ptr(dk), _ptr(dv), *dims, float(scale), int(bool(causal)),
+                        _dtype_code(q), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dq, dk, dv
+
+
+def attn_bwd_local(q, k, v, o, do, lse, scale, window_left, window_right, dq=None, dk=None,
+                   dv=None, workspace=None, stream=None):
+    """attn_bwd for the band of attn_fwd_local."""
+    lib = load_library()
+    dims, dq, dk, dv, workspace = _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace)
+    _check(lib.attn_bwd_local(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                              _ptr(dq), _ptr(dk), _ptr(dv), *dims, float(scale),
+                              int(window_left), int(window_right), _dtype_code(q),
+                              _ptr(workspace), workspace.numel(), _stream(stream)))
     return dq, dk, dv
 
 

@@ -72,7 +72,19 @@ attn_status_t check_fwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, floa
   if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension %d not in {64,128}", d);
   const long long rows = (long long)B * H * Nq;
   if (rows * d > (1LL << 46)) return fail(ATTN_ERR_INVALID_ARG, "tensor too large");
+  // One head's rows are addressed with 32-bit byte offsets.
+  const long long elt = dtype == ATTN_DTYPE_BF16 ? 2 : 4;
+  if ((long long)(Nq > Nk ? Nq : Nk) * d * elt >= (1LL << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "sequence too long: one head's rows exceed 2 GiB");
   return ATTN_OK;
+}
+
+// Window sides as the kernels take them: -1 (no limit) becomes kUnbounded.
+bool window_sides(int window_left, int window_right, int* left, int* right) {
+  if (window_left < -1 || window_right < -1) return false;
+  *left = window_left < 0 ? eta::kUnbounded : window_left;
+  *right = window_right < 0 ? eta::kUnbounded : window_right;
+  return true;
 }
 
 // ----------------------------------------------------------------- decode
@@ -126,24 +138,73 @@ attn_status_t check_bwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, floa
   return ATTN_OK;
 }
 
-}  // namespace
 
-extern "C" {
-
-attn_status_t attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
-                       int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+attn_status_t fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                       int H, int Hkv, int Nq, int Nk, int d, float scale, int left, int right,
                        attn_dtype_t dtype, void* stream) {
   if (!Q || !K || !V || !O || !LSE) return fail(ATTN_ERR_INVALID_ARG, "null tensor pointer");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
     return fail(ATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   attn_status_t st = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale, dtype);
   if (st != ATTN_OK) return st;
-  eta::FwdArgs a{Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, causal, dtype == ATTN_DTYPE_BF16};
+  const bool band = left != eta::kUnbounded || right != eta::kUnbounded;
+  const bool causal = left == eta::kUnbounded && right == 0;
+  if (dtype == ATTN_DTYPE_F32 && band && !causal)
+    return fail(ATTN_ERR_UNSUPPORTED, "fp32 forward supports only the causal or no mask");
+  eta::FwdArgs a{Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, causal ? 1 : 0, band ? 1 : 0,
+                 left, right, dtype == ATTN_DTYPE_BF16};
   eta::FwdPlan p = plan_fwd(B, H, Nq, d, a.dtype_bf16);
   if (p.workgroups > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "grid too large");
   hipError_t e = eta::launch_fwd(a, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+attn_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                       const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv,
+                       int Nq, int Nk, int d, float scale, int left, int right,
+                       attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV)
+    return fail(ATTN_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
+    return fail(ATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  attn_status_t st = check_bwd_shape(B, H, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  const size_t need = eta::bwd_workspace_bytes(B, H, Nq, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "backward workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const bool band = left != eta::kUnbounded || right != eta::kUnbounded;
+  eta::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Hkv, Nq, Nk, d, scale, band ? 1 : 0,
+                 left, right, workspace};
+  hipError_t e = eta::launch_bwd(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+
+attn_status_t attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                       int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                       attn_dtype_t dtype, void* stream) {
+  return fwd_impl(Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, eta::kUnbounded,
+                  causal ? 0 : eta::kUnbounded, dtype, stream);
+}
+
+attn_status_t attn_fwd_local(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                             int window_left, int window_right, attn_dtype_t dtype,
+                             void* stream) {
+  int left, right;
+  if (!window_sides(window_left, window_right, &left, &right))
+    return fail(ATTN_ERR_INVALID_ARG, "window sides must be >= -1 (got %d, %d)", window_left,
+                window_right);
+  return fwd_impl(Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, left, right, dtype, stream);
 }
 
 size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_context,
@@ -221,22 +282,21 @@ attn_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* 
                        const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv,
                        int Nq, int Nk, int d, float scale, int causal, attn_dtype_t dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV)
-    return fail(ATTN_ERR_INVALID_ARG, "null tensor pointer");
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
-      !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
-    return fail(ATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-  attn_status_t st = check_bwd_shape(B, H, Hkv, Nq, Nk, d, scale, dtype);
-  if (st != ATTN_OK) return st;
-  const size_t need = eta::bwd_workspace_bytes(B, H, Nq, d);
-  if (!workspace || workspace_bytes < need)
-    return fail(ATTN_ERR_WORKSPACE, "backward workspace needs %zu bytes, got %zu", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  eta::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Hkv, Nq, Nk, d, scale, causal, workspace};
-  hipError_t e = eta::launch_bwd(a, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Hkv, Nq, Nk, d, scale, eta::kUnbounded,
+                  causal ? 0 : eta::kUnbounded, dtype, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_bwd_local(const void* Q, const void* K, const void* V, const void* O,
+                             const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B,
+                             int H, int Hkv, int Nq, int Nk, int d, float scale, int window_left,
+                             int window_right, attn_dtype_t dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  int left, right;
+  if (!window_sides(window_left, window_right, &left, &right))
+    return fail(ATTN_ERR_INVALID_ARG, "window sides must be >= -1 (got %d, %d)", window_left,
+                window_right);
+  return bwd_impl(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Hkv, Nq, Nk, d, scale, left, right,
+                  dtype, workspace, workspace_bytes, stream);
 }
 
 int attn_plan_describe(int phase, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,

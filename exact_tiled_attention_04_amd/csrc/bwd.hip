@@ -31,7 +31,8 @@
 //
 // Rows past Nq or Nk arrive as zeros from the buffer loads.  A zero query
 // row has dO = 0 and adds nothing to dK or dV, so the dK/dV kernel applies
-// only the causal mask; the dQ kernel also masks keys past Nk (see there).
+// only the band (causal or local) mask; the dQ kernel also masks keys past
+// Nk (see there).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -83,13 +84,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 
 // ----------------------------------------------------------------- dK, dV
 
-template <int D, bool CAUSAL>
+template <int D, bool BAND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETA_BWD_KV_WAVES_PER_EU)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ LSE2, const float* __restrict__ Dsum,
                      __bf16* __restrict__ dK, __bf16* __restrict__ dV, int B, int H, int Hkv,
-                     int Nq, int Nk, float scale, float scale_log2) {
+                     int Nq, int Nk, float scale, float scale_log2, int win_left,
+                     int win_right) {
   constexpr int NT = 256;
   constexpr int CH = D / 8;
   constexpr int KS = D / 16;
@@ -131,14 +133,18 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     vf[ks] = __builtin_bit_cast(bf16x8, buf_load16(vrs, jw * ROW + (16 * ks + 8 * hh) * 2, 0));
   }
 
-  // Query tiles that can see this key tile, for each head of the group.
+  // Query tiles that can see this key tile, for each head of the group:
+  // query i (position i + off) sees key j iff j - win_right <= i + off <=
+  // j + win_left.
   const int n_qt = (Nq + kBQ - 1) / kBQ;
-  int qt_begin = 0;
-  if (CAUSAL) {
-    const int first_q = j0 - off;  // first query row that sees key j0
-    qt_begin = first_q <= 0 ? 0 : first_q / kBQ;
+  int qt_begin = 0, qt_end = n_qt - 1;
+  if (BAND) {
+    const int i_lo = max(0, j0 - win_right - off);
+    const int i_hi = min(Nq - 1, j0 + kBK - 1 + win_left - off);
+    qt_begin = i_lo / kBQ;
+    qt_end = i_lo <= i_hi ? i_hi / kBQ : qt_begin - 1;
   }
-  const int per_head = n_qt > qt_begin ? n_qt - qt_begin : 0;
+  const int per_head = qt_end >= qt_begin ? qt_end - qt_begin + 1 : 0;
   const int n_iter = per_head * G;
 
   // Loop-invariant byte offsets (the same scheme as the forward).
@@ -198,7 +204,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const char* Os = cur + QT;
     const float* lse2 = (const float*)(cur + STAT);
     const float* dsum = lse2 + kBQ;
-    const bool need_mask = CAUSAL && (j0 + 32 * wave + 31 > q0 + off);
+    const bool need_mask = BAND && (j0 + 32 * wave + 31 > q0 + off + win_right ||
+                                    j0 + 32 * wave < q0 + kBQ - 1 + off - win_left);
 
     bf16x8 pb[2][2], sb[2][2];
 #pragma unroll
@@ -221,7 +228,10 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
           float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[e]));
-          if (need_mask && jw > q0 + rloc + e + off) p = 0.f;
+          if (need_mask) {
+            const int pos = q0 + rloc + e + off;
+            if (jw > pos + win_right || jw < pos - win_left) p = 0.f;
+          }
           s[r] = p;
           dp[r] = p * (dp[r] - d4[e]) * scale;
         }
@@ -288,13 +298,13 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
 // --------------------------------------------------------------------- dQ
 
-template <int D, bool CAUSAL>
+template <int D, bool BAND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETA_BWD_Q_WAVES_PER_EU)))
 void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                    const float* __restrict__ LSE2, const float* __restrict__ Dsum,
                    __bf16* __restrict__ dQ, int B, int H, int Hkv, int Nq, int Nk, float scale,
-                   float scale_log2, int n_qtiles) {
+                   float scale_log2, int n_qtiles, int win_left, int win_right) {
   constexpr int NT = 256;
   constexpr int CH = D / 8;
   constexpr int KS = D / 16;
@@ -325,12 +335,14 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int qrow = q0 + 32 * wave + li;
   const int wave_row_lo = q0 + 32 * wave;
 
-  int n_tiles;
-  if (CAUSAL) {
-    const int last = min(Nk - 1, q0 + kBR - 1 + off);
-    n_tiles = last < 0 ? 0 : last / kBC + 1;
+  int t_lo = 0, t_hi;  // key tiles this query tile sees (as in the forward)
+  if (BAND) {
+    const int k_lo = max(0, q0 + off - win_left);
+    const int k_hi = min(Nk - 1, min(q0 + kBR, Nq) - 1 + off + win_right);
+    t_lo = k_lo / kBC;
+    t_hi = k_lo <= k_hi ? k_hi / kBC : t_lo - 1;
   } else {
-    n_tiles = (Nk + kBC - 1) / kBC;
+    t_hi = (Nk + kBC - 1) / kBC - 1;
   }
 
   const size_t hq = ((size_t)b * H + h) * (size_t)Nq;
@@ -383,8 +395,9 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   auto step = [&](int t, const char* Ks, char* next) {
     const int k0 = t * kBC;
-    if (t + 1 < n_tiles) load_tile(t + 1, next);
-    const bool wave_live = !CAUSAL || (k0 <= wave_row_lo + 31 + off);
+    if (t + 1 <= t_hi) load_tile(t + 1, next);
+    const bool wave_live = !BAND || (k0 <= wave_row_lo + 31 + off + win_right &&
+                                     k0 + kBC - 1 >= wave_row_lo + off - win_left);
     if (wave_live) {
       const char* Vs = Ks + TILE;
       f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
@@ -395,11 +408,14 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           s[kb] = mfma32(*(const bf16x8*)(Ks + kb * 32 * ROW + kofs[ks]), qf[ks], s[kb]);
           dp[kb] = mfma32(*(const bf16x8*)(Vs + kb * 32 * ROW + kofs[ks]), of[ks], dp[kb]);
         }
-      // Causal boundary, and the ragged key tail: a zero key row past Nk
+      // Band edges, and the ragged key tail: a zero key row past Nk
       // would contribute P * 0, but P = 2^-LSE2 can overflow for rows whose
       // scores are all very negative, so those keys are masked to P = 0.
-      const bool need_mask = (k0 + kBC > Nk) || (CAUSAL && (k0 + kBC - 1 > wave_row_lo + off));
-      const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
+      const bool need_mask =
+          (k0 + kBC > Nk) || (BAND && (k0 + kBC - 1 > wave_row_lo + off + win_right ||
+                                       k0 < wave_row_lo + 31 + off - win_left));
+      const int lim = BAND ? min(Nk - 1, qrow + off + win_right) : Nk - 1;
+      const int lim_lo = BAND ? qrow + off - win_left : 0;
       bf16x8 sb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -408,7 +424,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -lse2));
           if (need_mask) {
             const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key > lim) p = 0.f;
+            if (key > lim || key < lim_lo) p = 0.f;
           }
           dp[kb][r] = p * (dp[kb][r] - dd) * scale;
         }
@@ -438,12 +454,12 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __syncthreads();
   };
 
-  if (n_tiles > 0) load_tile(0, sm0);
+  if (t_lo <= t_hi) load_tile(t_lo, sm0);
   wait_vmem();
   __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = t_lo; t <= t_hi; t += 2) {
     step(t, sm0, sm1);
-    if (t + 1 < n_tiles) step(t + 1, sm1, sm0);
+    if (t + 1 <= t_hi) step(t + 1, sm1, sm0);
   }
 
   // Lane (query qrow, hh) register r of block nb holds column 32 nb + 8 (r/4) + 4 hh + r%4.
@@ -462,22 +478,22 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool BAND>
 hipError_t launch_main(const BwdArgs& a, const float* lse2, const float* dsum,
                        hipStream_t stream) {
   const float sl2 = a.scale * kLog2e;
   const int n_kt = (a.Nk + kBK - 1) / kBK;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(n_kt * a.B * a.Hkv)), dim3(256),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BAND>), dim3((unsigned)(n_kt * a.B * a.Hkv)), dim3(256),
                      0, stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
                      (const __bf16*)a.dO, lse2, dsum, (__bf16*)a.dK, (__bf16*)a.dV, a.B, a.H,
-                     a.Hkv, a.Nq, a.Nk, a.scale, sl2);
+                     a.Hkv, a.Nq, a.Nk, a.scale, sl2, a.win_left, a.win_right);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qt = (a.Nq + kBR - 1) / kBR;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(n_qt * a.B * a.H)), dim3(256), 0,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BAND>), dim3((unsigned)(n_qt * a.B * a.H)), dim3(256), 0,
                      stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
                      (const __bf16*)a.dO, lse2, dsum, (__bf16*)a.dQ, a.B, a.H, a.Hkv, a.Nq, a.Nk,
-                     a.scale, sl2, n_qt);
+                     a.scale, sl2, n_qt, a.win_left, a.win_right);
   return hipGetLastError();
 }
 
@@ -491,8 +507,8 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
                      stream, (const __bf16*)a.O, (const __bf16*)a.dO, a.LSE, dsum, lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return a.causal ? launch_main<D, true>(a, lse2, dsum, stream)
-                  : launch_main<D, false>(a, lse2, dsum, stream);
+  return a.band ? launch_main<D, true>(a, lse2, dsum, stream)
+                : launch_main<D, false>(a, lse2, dsum, stream);
 }
 
 }  // namespace

@@ -51,12 +51,13 @@ constexpr int fwd_bc() { return D == 128 ? 32 : 64; }
 constexpr float kSlack = 8.f;
 
 
-template <int D, bool CAUSAL, int NW, int BC>
+template <int D, bool BAND, int NW, int BC>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BC == 32 ? 3 : 2)))
 void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
-    int B, int H, int Hkv, int Nq, int Nk, float scale_log2, int n_qtiles) {
+    int B, int H, int Hkv, int Nq, int Nk, float scale_log2, int n_qtiles, int win_left,
+    int win_right) {
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;
   constexpr int CH = D / 8;                  // 16-byte chunks per row
@@ -101,13 +102,18 @@ void fwd_bf16_kernel(
   const int qrow = q0 + wave * 32 + li;
   const int wave_row_lo = q0 + wave * 32;
 
-  // Number of key tiles this query tile can see.
-  int n_tiles;
-  if (CAUSAL) {
-    int last = min(Nk - 1, q0 + BR - 1 + off);
-    n_tiles = last < 0 ? 0 : last / BC + 1;
+  // Key tiles this query tile can see: t_lo .. t_hi.  With a band, the rows
+  // of the tile see keys from (first position - win_left) to (last position
+  // + win_right); causal is the band (unbounded, 0) ("Kernel structure":
+  // causal and local masks change the visited tile range).
+  int t_lo = 0, t_hi;
+  if (BAND) {
+    const int k_lo = max(0, q0 + off - win_left);
+    const int k_hi = min(Nk - 1, min(q0 + BR, Nq) - 1 + off + win_right);
+    t_lo = k_lo / BC;
+    t_hi = k_lo <= k_hi ? k_hi / BC : t_lo - 1;
   } else {
-    n_tiles = (Nk + BC - 1) / BC;
+    t_hi = (Nk + BC - 1) / BC - 1;
   }
 
   // Queries of this lane's row as the B operand (Q^T); rows past Nq read 0.
@@ -158,9 +164,10 @@ void fwd_bf16_kernel(
 
   auto step = [&](int t, const char* Ks, char* next) {
     const int k0 = t * BC;
-    if (t + 1 < n_tiles) load_tile(t + 1, next);
-    // Tiles wholly above this wave's diagonal contribute nothing.
-    const bool wave_live = !CAUSAL || (k0 <= wave_row_lo + 31 + off);
+    if (t + 1 <= t_hi) load_tile(t + 1, next);
+    // Tiles wholly outside this wave's band contribute nothing.
+    const bool wave_live = !BAND || (k0 <= wave_row_lo + 31 + off + win_right &&
+                                     k0 + BC - 1 >= wave_row_lo + off - win_left);
     if (wave_live) {
       const char* Vs = Ks + TILE;
       // S^T for keys 32 kb .. 32 kb + 31 (s[kb]); with two blocks the
@@ -185,16 +192,19 @@ void fwd_bf16_kernel(
         for (int kb = 0; kb < KB; ++kb) a[kb] = n[kb];
       }
 
-      // Mask the causal boundary and the ragged key tail.
-      const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > wave_row_lo + off));
+      // Mask the band's edges and the ragged key tail.
+      const bool need_mask =
+          (k0 + BC > Nk) || (BAND && (k0 + BC - 1 > wave_row_lo + off + win_right ||
+                                      k0 < wave_row_lo + 31 + off - win_left));
       if (need_mask) {
-        const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
+        const int lim = BAND ? min(Nk - 1, qrow + off + win_right) : Nk - 1;
+        const int lim_lo = BAND ? qrow + off - win_left : 0;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key > lim) s[kb][r] = -INFINITY;
+            if (key > lim || key < lim_lo) s[kb][r] = -INFINITY;
           }
       }
 
@@ -260,13 +270,13 @@ void fwd_bf16_kernel(
     __syncthreads();
   };
 
-  if (n_tiles > 0) load_tile(0, smem0);
+  if (t_lo <= t_hi) load_tile(t_lo, smem0);
   wait_vmem();
   __syncthreads();
   // Unrolled by two so each step's LDS buffers are fixed objects.
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = t_lo; t <= t_hi; t += 2) {
     step(t, smem0, smem1);
-    if (t + 1 < n_tiles) step(t + 1, smem1, smem0);
+    if (t + 1 <= t_hi) step(t + 1, smem1, smem0);
   }
 
   // Epilogue: one division per row, O in bf16, LSE in natural log.
@@ -437,7 +447,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool BAND>
 hipError_t launch_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
   const int br = p.block_rows;
   const int n_qtiles = (a.Nq + br - 1) / br;
@@ -448,11 +458,11 @@ hipError_t launch_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
   const __bf16* v = (const __bf16*)a.V;
   __bf16* o = (__bf16*)a.O;
   if (p.waves == 4) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, fwd_bc<D>()>), grid, dim3(256), 0, stream, q, k,
-                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 4, fwd_bc<D>()>), grid, dim3(256), 0, stream, q, k,
+                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, a.win_left, a.win_right);
   } else {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 2, fwd_bc<D>()>), grid, dim3(128), 0, stream, q, k,
-                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 2, fwd_bc<D>()>), grid, dim3(128), 0, stream, q, k,
+                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, a.win_left, a.win_right);
   }
   return hipGetLastError();
 }
@@ -473,9 +483,8 @@ hipError_t launch_f32(const FwdArgs& a, hipStream_t stream) {
 hipError_t launch_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
   if (a.dtype_bf16) {
     if (a.d == 128)
-      return a.causal ? launch_bf16<128, true>(a, p, stream)
-                      : launch_bf16<128, false>(a, p, stream);
-    return a.causal ? launch_bf16<64, true>(a, p, stream) : launch_bf16<64, false>(a, p, stream);
+      return a.band ? launch_bf16<128, true>(a, p, stream) : launch_bf16<128, false>(a, p, stream);
+    return a.band ? launch_bf16<64, true>(a, p, stream) : launch_bf16<64, false>(a, p, stream);
   }
   if (a.d == 128)
     return a.causal ? launch_f32<128, true>(a, stream) : launch_f32<128, false>(a, stream);

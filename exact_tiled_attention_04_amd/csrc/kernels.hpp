@@ -7,6 +7,9 @@
 
 namespace eta {
 
+// A window side with no limit (larger than any sequence the library accepts).
+constexpr int kUnbounded = 1 << 30;
+
 struct FwdArgs {
   const void* Q;
   const void* K;
@@ -15,7 +18,12 @@ struct FwdArgs {
   float* LSE;
   int B, H, Hkv, Nq, Nk, d;
   float scale;
-  int causal;
+  int causal;          // fp32 path: causal mask or none
+  // Banded mask (bf16 path): key j is visible from query position p (bottom-
+  // right aligned) iff p - win_left <= j <= p + win_right; kUnbounded on a
+  // side means no limit there.  causal = (kUnbounded, 0).
+  int band;            // 0: every key visible (win_* ignored)
+  int win_left, win_right;
   bool dtype_bf16;
 };
 
@@ -58,7 +66,8 @@ struct BwdArgs {
   void* dV;
   int B, H, Hkv, Nq, Nk, d;
   float scale;
-  int causal;
+  int band;            // as in FwdArgs
+  int win_left, win_right;
   void* workspace;
 };
 

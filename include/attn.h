@@ -34,7 +34,9 @@
  *     is float32, outputs are rounded to nearest even.  ATTN_DTYPE_F32: all
  *     float32 (forward only).
  *   - Head dimension d must be 64 or 128.  H must be a multiple of Hkv; query
- *     head h reads KV head h / (H / Hkv) (contiguous groups).
+ *     head h reads KV head h / (H / Hkv) (contiguous groups).  One head's
+ *     rows (N * d * element size) must stay below 2 GiB (32-bit offsets;
+ *     else ATTN_ERR_UNSUPPORTED).
  *   - causal != 0 applies the causal mask aligned to the bottom-right corner:
  *     query row i may see key j iff j <= i + (Nk - Nq).  A row that sees no
  *     key gets O = 0 and LSE = -inf.
@@ -82,6 +84,27 @@ typedef enum { ATTN_PHASE_FWD = 0, ATTN_PHASE_DECODE = 1, ATTN_PHASE_BWD = 2 } a
 attn_status_t attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
                        int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                        attn_dtype_t dtype, void* stream);
+
+/*
+ * Forward with a local (banded) mask.  "Modern attention kernels", "Kernel
+ * structure": local attention changes the range of key tiles a query tile
+ * visits; "Attention kernels", sparse-attention paragraph: a sliding window
+ * lets each position see a fixed number of recent positions.
+ *   Query row i sits at position p = i + (Nk - Nq) (bottom-right alignment, as
+ *   for causal) and sees key j iff p - window_left <= j <= p + window_right.
+ *   window_left, window_right >= 0, or -1 for no limit on that side:
+ *     (-1, 0)  = the causal mask (same result as attn_fwd with causal = 1);
+ *     (W-1, 0) = a causal sliding window of W keys;
+ *     (-1, -1) = no mask.
+ *   A row whose band holds no key gets O = 0, LSE = -inf.  Other arguments
+ *   and errors as attn_fwd; with dtype F32 only (-1, 0) and (-1, -1) are
+ *   supported (else ATTN_ERR_UNSUPPORTED); a side below -1 gives
+ *   ATTN_ERR_INVALID_ARG.
+ */
+attn_status_t attn_fwd_local(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                             int window_left, int window_right, attn_dtype_t dtype,
+                             void* stream);
 
 /*
  * Bytes of workspace attn_decode_paged needs for these sizes (0 when the
@@ -156,6 +179,18 @@ attn_status_t attn_bwd(const void* Q, const void* K, const void* V, const void* 
                        const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv,
                        int Nq, int Nk, int d, float scale, int causal, attn_dtype_t dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of attn_fwd_local by recomputation, for the same band
+ * (window_left, window_right as there; O and LSE must come from
+ * attn_fwd_local with the same band).  Other arguments, workspace and errors
+ * as attn_bwd.
+ */
+attn_status_t attn_bwd_local(const void* Q, const void* K, const void* V, const void* O,
+                             const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B,
+                             int H, int Hkv, int Nq, int Nk, int d, float scale, int window_left,
+                             int window_right, attn_dtype_t dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * Describe the kernel choice for a phase and shape ("Modern attention

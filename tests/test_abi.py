@@ -157,3 +157,28 @@ def test_tensor_marshalling_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.attn_fwd(q, q, q, 0.125, True)
+
+
+def _fwd_local(lib, left, right, dtype=attn.ATTN_DTYPE_BF16, Nq=8, Nk=8, d=64):
+    return lib.attn_fwd_local(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, Nq, Nk, d, 0.125, left, right,
+                              dtype, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(left=-2, right=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(left=0, right=-5), attn.ATTN_ERR_INVALID_ARG),
+    (dict(left=3, right=0, dtype=attn.ATTN_DTYPE_F32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(left=-1, right=2, dtype=attn.ATTN_DTYPE_F32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(left=3, right=0, Nk=1 << 23, d=128), attn.ATTN_ERR_UNSUPPORTED),  # > 2 GiB per head
+])
+def test_fwd_local_validation(lib, cpu_only, kw, status):
+    assert _fwd_local(lib, **kw) == status
+
+
+def test_bwd_local_validation(lib, cpu_only):
+    st = lib.attn_bwd_local(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 16, 16,
+                            64, 0.1, -3, 0, attn.ATTN_DTYPE_BF16, FAKE, 1 << 20, NULL)
+    assert st == attn.ATTN_ERR_INVALID_ARG
+    st = lib.attn_bwd_local(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 16, 16,
+                            64, 0.1, 4, 0, attn.ATTN_DTYPE_BF16, FAKE, 16, NULL)
+    assert st == attn.ATTN_ERR_WORKSPACE
