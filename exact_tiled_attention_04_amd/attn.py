@@ -7,7 +7,8 @@ in the library's HIP kernels.  There is no fallback: if the library has not
 been built (``python -m exact_tiled_attention_04_amd.build``) the first call
 raises.
 
-Names follow the C ABI: ``attn_fwd``, ``attn_fwd_local``, ``attn_decode_paged``,
+Names follow the C ABI: ``attn_fwd``, ``attn_fwd_local``, ``attn_fwd_splitkv``,
+``attn_fwd_splitkv_workspace_size``, ``attn_decode_paged``,
 ``attn_bwd``, ``attn_bwd_local``, ``attn_decode_paged_workspace_size``,
 ``attn_bwd_workspace_size``, ``attn_plan_describe``, ``attn_status_string``.
 """
@@ -35,6 +36,8 @@ ATTN_PHASE_BWD = 2
 EXPORTED = (
     "attn_fwd",
     "attn_fwd_local",
+    "attn_fwd_splitkv_workspace_size",
+    "attn_fwd_splitkv",
     "attn_bwd_local",
     "attn_decode_paged_workspace_size",
     "attn_decode_paged",
@@ -73,6 +76,11 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd_local.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                    i32, vp]
     lib.attn_fwd_local.restype = i32
+    lib.attn_fwd_splitkv_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.attn_fwd_splitkv_workspace_size.restype = sz
+    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                     i32, i32, i32, vp, sz, vp]
+    lib.attn_fwd_splitkv.restype = i32
     lib.attn_decode_paged_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_decode_paged_workspace_size.restype = sz
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -168,6 +176,32 @@ def attn_fwd_local(q, k, v, scale, window_left, window_right, out=None, lse=None
     _check(lib.attn_fwd_local(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *dims,
                               float(scale), int(window_left), int(window_right), _dtype_code(q),
                               _stream(stream)))
+    return out, lse
+
+
+def attn_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, window_left=-1, window_right=-1,
+                                    chunk_keys=0):
+    return int(load_library().attn_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, window_left,
+                                                              window_right, chunk_keys))
+
+
+def attn_fwd_splitkv(q, k, v, scale, window_left=-1, window_right=-1, chunk_keys=0, out=None,
+                     lse=None, workspace=None, stream=None):
+    """attn_fwd_local whose query tiles may split their key range over several
+    workgroups (chunk_keys = 0: the library decides; the split needs the
+    workspace of attn_fwd_splitkv_workspace_size, which is 0 when it does not
+    split)."""
+    lib = load_library()
+    dims, out, lse = _fwd_args(q, k, v, out, lse)
+    B, H, _, Nq, Nk, d = dims
+    need = attn_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, window_left, window_right,
+                                           chunk_keys)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *dims,
+                                float(scale), int(window_left), int(window_right),
+                                _dtype_code(q), int(chunk_keys), _ptr(workspace),
+                                0 if workspace is None else workspace.numel(), _stream(stream)))
     return out, lse
 
 

@@ -139,9 +139,53 @@ attn_status_t check_bwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, floa
 }
 
 
+// Key split of the bf16 forward ("Work partitioning in FlashAttention-2":
+// too few independent workgroups leave CUs idle; "Attention kernels",
+// FlashDecoding paragraph: split the key range and merge the partials).
+// When B*H*ceil(Nq/128) query tiles give fewer than two workgroups per CU,
+// each tile's key range is cut into chunks sized for about six workgroups per
+// CU in total (at least 256 keys each).  chunk_keys > 0 forces that chunk.
+struct SplitPlan {
+  int chunk_tiles = 0;
+  int n_chunks = 0;  // 0: no split
+  size_t ws = 0;
+};
+
+SplitPlan plan_fwd_split(int B, int H, int Nq, int Nk, int d, int left, int right,
+                         int chunk_keys) {
+  SplitPlan sp;
+  const int bc = eta::fwd_tile_keys(d);
+  const int n_qt = (Nq + 127) / 128;
+  const bool band = left != eta::kUnbounded || right != eta::kUnbounded;
+  int ct;
+  if (chunk_keys > 0) {
+    ct = (chunk_keys + bc - 1) / bc;
+  } else {
+    if ((long long)B * H * n_qt >= 2LL * kNumCU) return sp;
+    long long work = 0;
+    for (int qt = 0; qt < n_qt; ++qt) {
+      int lo, hi;
+      eta::band_tiles(band, qt * 128, 128, Nq, Nk, bc, left, right, lo, hi);
+      if (hi >= lo) work += hi - lo + 1;
+    }
+    work *= (long long)B * H;
+    const long long target = 6LL * kNumCU;
+    ct = (int)((work + target - 1) / target);
+    if (ct < 256 / bc) ct = 256 / bc;
+  }
+  const int n_tiles = (Nk + bc - 1) / bc;
+  const int n_chunks = (n_tiles + ct - 1) / ct;
+  if (n_chunks <= 1 && chunk_keys == 0) return sp;
+  sp.chunk_tiles = ct;
+  sp.n_chunks = n_chunks;
+  sp.ws = (size_t)B * H * n_qt * n_chunks * 128 * (size_t)(d + 2) * sizeof(float);
+  return sp;
+}
+
 attn_status_t fwd_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
                        int H, int Hkv, int Nq, int Nk, int d, float scale, int left, int right,
-                       attn_dtype_t dtype, void* stream) {
+                       attn_dtype_t dtype, void* stream, const SplitPlan& sp = SplitPlan(),
+                       void* workspace = nullptr) {
   if (!Q || !K || !V || !O || !LSE) return fail(ATTN_ERR_INVALID_ARG, "null tensor pointer");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
     return fail(ATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
@@ -151,10 +195,15 @@ attn_status_t fwd_impl(const void* Q, const void* K, const void* V, void* O, flo
   const bool causal = left == eta::kUnbounded && right == 0;
   if (dtype == ATTN_DTYPE_F32 && band && !causal)
     return fail(ATTN_ERR_UNSUPPORTED, "fp32 forward supports only the causal or no mask");
+  if (dtype == ATTN_DTYPE_F32 && sp.n_chunks > 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "the key split is bf16 only");
   eta::FwdArgs a{Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, causal ? 1 : 0, band ? 1 : 0,
-                 left, right, dtype == ATTN_DTYPE_BF16};
+                 left, right, dtype == ATTN_DTYPE_BF16, sp.chunk_tiles, sp.n_chunks, workspace};
   eta::FwdPlan p = plan_fwd(B, H, Nq, d, a.dtype_bf16);
-  if (p.workgroups > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "grid too large");
+  const long long grid = sp.n_chunks > 0
+                             ? (long long)B * H * ((Nq + 127) / 128) * sp.n_chunks
+                             : p.workgroups;
+  if (grid > kMaxGrid) return fail(ATTN_ERR_INVALID_ARG, "grid too large");
   hipError_t e = eta::launch_fwd(a, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -205,6 +254,41 @@ attn_status_t attn_fwd_local(const void* Q, const void* K, const void* V, void* 
     return fail(ATTN_ERR_INVALID_ARG, "window sides must be >= -1 (got %d, %d)", window_left,
                 window_right);
   return fwd_impl(Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, left, right, dtype, stream);
+}
+
+size_t attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int window_left,
+                                       int window_right, int chunk_keys) {
+  int left, right;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128) || chunk_keys < 0 ||
+      chunk_keys % 64 != 0 || !window_sides(window_left, window_right, &left, &right))
+    return 0;
+  return plan_fwd_split(B, H, Nq, Nk, d, left, right, chunk_keys).ws;
+}
+
+attn_status_t attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                               int window_left, int window_right, attn_dtype_t dtype,
+                               int chunk_keys, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  int left, right;
+  if (!window_sides(window_left, window_right, &left, &right))
+    return fail(ATTN_ERR_INVALID_ARG, "window sides must be >= -1 (got %d, %d)", window_left,
+                window_right);
+  if (chunk_keys < 0 || chunk_keys % 64 != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "chunk_keys=%d must be 0 or a positive multiple of 64",
+                chunk_keys);
+  attn_status_t st = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  const SplitPlan sp = plan_fwd_split(B, H, Nq, Nk, d, left, right, chunk_keys);
+  if (sp.n_chunks > 0) {
+    if (!workspace || workspace_bytes < sp.ws)
+      return fail(ATTN_ERR_WORKSPACE, "split forward workspace needs %zu bytes, got %zu", sp.ws,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace))
+      return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  return fwd_impl(Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, left, right, dtype, stream, sp,
+                  workspace);
 }
 
 size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_context,

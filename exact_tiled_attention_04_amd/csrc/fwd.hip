@@ -51,13 +51,13 @@ constexpr int fwd_bc() { return D == 128 ? 32 : 64; }
 constexpr float kSlack = 8.f;
 
 
-template <int D, bool BAND, int NW, int BC>
+template <int D, bool BAND, int NW, int BC, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BC == 32 ? 3 : 2)))
 void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
     int B, int H, int Hkv, int Nq, int Nk, float scale_log2, int n_qtiles, int win_left,
-    int win_right) {
+    int win_right, int chunk_tiles, int n_chunks, float* __restrict__ part) {
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;
   constexpr int CH = D / 8;                  // 16-byte chunks per row
@@ -85,8 +85,18 @@ void fwd_bf16_kernel(
 
   const int BH = B * H;
   const int wg = blockIdx.x;
-  const int qt = n_qtiles - 1 - wg / BH;  // heavy (late) query tiles first
-  const int bh = wg % BH;
+  // Heavy (late) query tiles first; with a key split, the chunks of one query
+  // tile follow each other (each over every head).
+  int qt, bh, chunk = 0;
+  if (SPLIT) {
+    const int per_qt = n_chunks * BH;
+    qt = n_qtiles - 1 - wg / per_qt;
+    chunk = (wg % per_qt) / BH;
+    bh = (wg % per_qt) % BH;
+  } else {
+    qt = n_qtiles - 1 - wg / BH;
+    bh = wg % BH;
+  }
   const int b = bh / H;
   const int h = bh % H;
   const int g = h / (H / Hkv);
@@ -106,14 +116,16 @@ void fwd_bf16_kernel(
   // of the tile see keys from (first position - win_left) to (last position
   // + win_right); causal is the band (unbounded, 0) ("Kernel structure":
   // causal and local masks change the visited tile range).
-  int t_lo = 0, t_hi;
-  if (BAND) {
-    const int k_lo = max(0, q0 + off - win_left);
-    const int k_hi = min(Nk - 1, min(q0 + BR, Nq) - 1 + off + win_right);
-    t_lo = k_lo / BC;
-    t_hi = k_lo <= k_hi ? k_hi / BC : t_lo - 1;
-  } else {
-    t_hi = (Nk + BC - 1) / BC - 1;
+  int t_lo, t_hi;
+  band_tiles(BAND, q0, BR, Nq, Nk, BC, win_left, win_right, t_lo, t_hi);
+  if (SPLIT) {
+    // This workgroup's share of the key range ("Attention kernels",
+    // FlashDecoding paragraph, applied to a prefill query tile): key tiles
+    // chunk * chunk_tiles .. + chunk_tiles - 1.  An empty share exits before
+    // any barrier (the condition is uniform over the workgroup).
+    t_lo = max(t_lo, chunk * chunk_tiles);
+    t_hi = min(t_hi, chunk * chunk_tiles + chunk_tiles - 1);
+    if (t_lo > t_hi) return;
   }
 
   // Queries of this lane's row as the B operand (Q^T); rows past Nq read 0.
@@ -279,8 +291,31 @@ void fwd_bf16_kernel(
     if (t + 1 <= t_hi) step(t + 1, smem1, smem0);
   }
 
-  // Epilogue: one division per row, O in bf16, LSE in natural log.
   const float l_tot = halves_sum(l_run);
+  if (SPLIT) {
+    // Unnormalised partial: o, the base-2 reference max and the sum, merged
+    // by fwd_merge_kernel.
+    if (qrow < Nq) {
+      const size_t prow = (((size_t)bh * n_qtiles + qt) * n_chunks + chunk) * BR + wave * 32 + li;
+      float* po = part + prow * D;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = o[nb][4 * r4 + e];
+          *(f32x4*)(po + 32 * nb + 8 * r4 + 4 * hh) = w;
+        }
+      if (hh == 0) {
+        float* pml = part + (size_t)BH * n_qtiles * n_chunks * BR * D + prow * 2;
+        pml[0] = m_run;
+        pml[1] = l_tot;
+      }
+    }
+    return;
+  }
+  // Epilogue: one division per row, O in bf16, LSE in natural log.
   if (qrow < Nq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __bf16* dst = Op + (size_t)qrow * D;
@@ -296,6 +331,61 @@ void fwd_bf16_kernel(
       }
     if (hh == 0) Lp[qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
   }
+}
+
+// Merge of one query row's key-split partials (the split-context algebra of
+// "Attention kernels", FlashDecoding paragraph): M = max_c m_c,
+// w_c = 2^(m_c - M), l = sum_c w_c l_c, O = sum_c w_c o_c / l,
+// LSE = (M + log2 l) ln 2.  One workgroup per (row, batch x head), one thread
+// per output column; the partial loads are issued eight chunks at a time.
+template <int D>
+__global__ __launch_bounds__(D) void fwd_merge_kernel(
+    const float* __restrict__ part, __bf16* __restrict__ O, float* __restrict__ LSE, int BH,
+    int Nq, int Nk, int n_qtiles, int n_chunks, int chunk_tiles, int band, int win_left,
+    int win_right) {
+  constexpr int BR = 128;
+  constexpr int BC = fwd_bc<D>();
+  constexpr int kBatch = 8;
+  const int row = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int n = threadIdx.x;
+  const int qt = row / BR;
+  int t_lo, t_hi;
+  band_tiles(band != 0, qt * BR, BR, Nq, Nk, BC, win_left, win_right, t_lo, t_hi);
+  const int c_lo = t_lo / chunk_tiles;
+  const int c_hi = t_lo <= t_hi ? t_hi / chunk_tiles : c_lo - 1;
+  const size_t row0 = ((size_t)bh * n_qtiles + qt) * n_chunks * BR + row % BR;
+  const float* ml = part + (size_t)BH * n_qtiles * n_chunks * BR * D;
+  float big_m = -INFINITY, acc = 0.f, ell = 0.f;
+  for (int c0 = c_lo; c0 <= c_hi; c0 += kBatch) {
+    float mv[kBatch], lv[kBatch], ov[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool ok = c0 + j <= c_hi;
+      const size_t prow = row0 + (size_t)(ok ? c0 + j : c_lo) * BR;
+      mv[j] = ok ? ml[prow * 2] : -INFINITY;
+      lv[j] = ok ? ml[prow * 2 + 1] : 0.f;
+      ov[j] = ok ? part[prow * D + n] : 0.f;
+    }
+    float bm = big_m;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) bm = fmaxf(bm, mv[j]);
+    if (bm == -INFINITY) continue;
+    const float r = fast_exp2(big_m - bm);
+    acc *= r;
+    ell *= r;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float w = fast_exp2(mv[j] - bm);
+      ell += w * lv[j];
+      acc += w * ov[j];
+    }
+    big_m = bm;
+  }
+  const float inv = ell > 0.f ? 1.f / ell : 0.f;
+  const size_t orow = (size_t)bh * Nq + row;
+  O[orow * D + n] = (__bf16)(acc * inv);
+  if (n == 0) LSE[orow] = ell > 0.f ? (big_m + fast_log2(ell)) * kLn2 : -INFINITY;
 }
 
 // fp32 path: the same tiling on v_mfma_f32_32x32x2f32 (P stays fp32).
@@ -449,20 +539,40 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(
 
 template <int D, bool BAND>
 hipError_t launch_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
+  constexpr int BC = fwd_bc<D>();
   const int br = p.block_rows;
   const int n_qtiles = (a.Nq + br - 1) / br;
-  dim3 grid((unsigned)(n_qtiles * a.B * a.H));
   const float sl2 = a.scale * kLog2e;
   const __bf16* q = (const __bf16*)a.Q;
   const __bf16* k = (const __bf16*)a.K;
   const __bf16* v = (const __bf16*)a.V;
   __bf16* o = (__bf16*)a.O;
+  if (a.n_chunks > 0) {
+    // Key split: always four waves, 128-row query tiles (whatever the
+    // unsplit plan's workgroup size), the tiling the host sized the
+    // workspace for; partials, then the merge.
+    const int n_qt = (a.Nq + 127) / 128;
+    float* part = (float*)a.workspace;
+    dim3 grid((unsigned)((long long)n_qt * a.n_chunks * a.B * a.H));
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 4, BC, true>), grid, dim3(256), 0, stream, q, k, v,
+                       o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qt, a.win_left,
+                       a.win_right, a.chunk_tiles, a.n_chunks, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fwd_merge_kernel<D>), dim3((unsigned)a.Nq, (unsigned)(a.B * a.H)),
+                       dim3(D), 0, stream, (const float*)part, o, a.LSE, a.B * a.H, a.Nq, a.Nk,
+                       n_qt, a.n_chunks, a.chunk_tiles, a.band, a.win_left, a.win_right);
+    return hipGetLastError();
+  }
+  dim3 grid((unsigned)(n_qtiles * a.B * a.H));
   if (p.waves == 4) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 4, fwd_bc<D>()>), grid, dim3(256), 0, stream, q, k,
-                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, a.win_left, a.win_right);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 4, BC, false>), grid, dim3(256), 0, stream, q, k,
+                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, a.win_left,
+                       a.win_right, 0, 0, nullptr);
   } else {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 2, fwd_bc<D>()>), grid, dim3(128), 0, stream, q, k,
-                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, a.win_left, a.win_right);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 2, BC, false>), grid, dim3(128), 0, stream, q, k,
+                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, a.win_left,
+                       a.win_right, 0, 0, nullptr);
   }
   return hipGetLastError();
 }

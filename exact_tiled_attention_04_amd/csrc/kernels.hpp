@@ -25,7 +25,34 @@ struct FwdArgs {
   int band;            // 0: every key visible (win_* ignored)
   int win_left, win_right;
   bool dtype_bf16;
+  // Key split (bf16 path; n_chunks = 0: none): each 128-row query tile's key
+  // tiles are cut into chunks of chunk_tiles tiles, computed as separate
+  // workgroups into `workspace` (fwd_split_workspace_bytes) and merged.
+  int chunk_tiles, n_chunks;
+  void* workspace;
 };
+
+// Key tiles of width BC seen by the query rows q0 .. q0 + rows - 1: t_lo .. t_hi
+// (empty when t_lo > t_hi).  With a band, the rows see keys from (first
+// position - win_left) to (last position + win_right), positions bottom-right
+// aligned; causal is the band (kUnbounded, 0).
+__host__ __device__ inline void band_tiles(bool band, int q0, int rows, int Nq, int Nk, int BC,
+                                           int win_left, int win_right, int& t_lo, int& t_hi) {
+  const int off = Nk - Nq;
+  if (band) {
+    const int last = (q0 + rows < Nq ? q0 + rows : Nq) - 1;
+    const int k_lo = q0 + off - win_left > 0 ? q0 + off - win_left : 0;
+    const int k_hi = last + off + win_right < Nk - 1 ? last + off + win_right : Nk - 1;
+    t_lo = k_lo / BC;
+    t_hi = k_lo <= k_hi ? k_hi / BC : t_lo - 1;
+  } else {
+    t_lo = 0;
+    t_hi = (Nk + BC - 1) / BC - 1;
+  }
+}
+
+// Key-tile width of the bf16 forward for head dimension d.
+inline int fwd_tile_keys(int d) { return d == 128 ? 32 : 64; }
 
 struct FwdPlan {
   int waves;        // waves per workgroup

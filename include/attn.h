@@ -107,6 +107,37 @@ attn_status_t attn_fwd_local(const void* Q, const void* K, const void* V, void* 
                              void* stream);
 
 /*
+ * Bytes of workspace attn_fwd_splitkv needs (0 when it will not split the
+ * key range for these sizes, or when the arguments are invalid).  Window
+ * sides and chunk_keys as for attn_fwd_splitkv.
+ */
+size_t attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int window_left,
+                                       int window_right, int chunk_keys);
+
+/*
+ * attn_fwd_local for grids too small to fill the GPU: each 128-row query tile
+ * may cut its key range into chunks computed by separate workgroups, whose
+ * unnormalised partials (o, max, sum) are merged by max-rescaling.  "Modern
+ * attention kernels", "Work partitioning in FlashAttention-2" (a grid with
+ * too few independent programs leaves hardware idle); "Attention kernels",
+ * FlashDecoding paragraph (split the keys, merge the partials exactly).
+ *   chunk_keys   0: the library splits only when B*H*ceil(Nq/128) < 512 and
+ *                chooses the chunk; > 0 (a multiple of 64): always split into
+ *                chunks of that many keys (rounded up to whole key tiles).
+ *   workspace    device scratch of attn_fwd_splitkv_workspace_size(...) bytes
+ *                (16-byte aligned; may be NULL when that size is 0).
+ * The result equals attn_fwd_local's within rounding (the order of the
+ * floating-point sums differs).  dtype must be BF16 when a split happens.
+ * Errors as attn_fwd_local, plus ATTN_ERR_INVALID_ARG for a bad chunk_keys
+ * and ATTN_ERR_WORKSPACE for a missing or short workspace.
+ */
+attn_status_t attn_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               int B, int H, int Hkv, int Nq, int Nk, int d, float scale,
+                               int window_left, int window_right, attn_dtype_t dtype,
+                               int chunk_keys, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * Bytes of workspace attn_decode_paged needs for these sizes (0 when the
  * arguments are invalid).  chunk_tokens as for attn_decode_paged.
  */

@@ -182,3 +182,28 @@ def test_bwd_local_validation(lib, cpu_only):
     st = lib.attn_bwd_local(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 16, 16,
                             64, 0.1, 4, 0, attn.ATTN_DTYPE_BF16, FAKE, 16, NULL)
     assert st == attn.ATTN_ERR_WORKSPACE
+
+
+def test_fwd_splitkv_workspace_queries(lib):
+    # Forced 256-key chunks over 1000 keys of d = 128 (32-key tiles): 4 chunks.
+    assert attn.attn_fwd_splitkv_workspace_size(1, 2, 1000, 1000, 128, -1, 0, 256) == \
+        2 * 8 * 4 * 128 * 130 * 4
+    assert attn.attn_fwd_splitkv_workspace_size(1, 2, 1000, 1000, 128, -1, 0, 100) == 0
+    assert attn.attn_fwd_splitkv_workspace_size(1, 32, 8192, 8192, 128, -1, 0, 0) == 0
+    assert attn.attn_fwd_splitkv_workspace_size(1, 4, 8192, 8192, 128, -1, 0, 0) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(chunk=100), attn.ATTN_ERR_INVALID_ARG),
+    (dict(chunk=-64), attn.ATTN_ERR_INVALID_ARG),
+    (dict(chunk=256, ws=NULL), attn.ATTN_ERR_WORKSPACE),
+    (dict(chunk=256, ws_bytes=16), attn.ATTN_ERR_WORKSPACE),
+    (dict(chunk=256, dtype=attn.ATTN_DTYPE_F32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(left=-4), attn.ATTN_ERR_INVALID_ARG),
+])
+def test_fwd_splitkv_validation(lib, cpu_only, kw, status):
+    chunk = kw.get("chunk", 0)
+    st = lib.attn_fwd_splitkv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 1000, 1000, 128, 0.1,
+                              kw.get("left", -1), 0, kw.get("dtype", attn.ATTN_DTYPE_BF16), chunk,
+                              kw.get("ws", FAKE), kw.get("ws_bytes", 1 << 30), NULL)
+    assert st == status
