@@ -119,6 +119,18 @@ def main():
     sum_ctx = int(dec["context_lens"].sum())
     dec_bytes = 2.0 * sum_ctx * dw["Hkv"] * dw["d"] * 2
 
+    # The four-head variant of the same prefill: too few query tiles to fill
+    # the chip, so it goes through the key split (partials + merge).
+    sw = workloads.WORKLOADS["causal_bf16_b1_h4_n8192_d128"]
+    sq, sk, sv = workloads.prefill(sw["B"], sw["H"], sw["Hkv"], sw["Nq"], sw["Nk"], sw["d"],
+                                   dtype="bf16", seed=sw["seed"], device=str(dev))
+    so = torch.empty_like(sq)
+    slse = torch.empty((sw["B"], sw["H"], sw["Nq"]), dtype=torch.float32, device=dev)
+    sws_bytes = attn.attn_fwd_splitkv_workspace_size(sw["B"], sw["H"], sw["Nq"], sw["Nk"],
+                                                     sw["d"], -1, 0, 0)
+    sws = torch.empty(max(sws_bytes, 16), dtype=torch.uint8, device=dev)
+    split_flops = 4.0 * sw["B"] * sw["H"] * sw["Nq"] * sw["Nk"] * sw["d"] / 2.0
+
     bw = workloads.WORKLOADS["causal_bwd_bf16_b2_h16_n4096_d128"]
     bq, bk, bv, bdo = workloads.backward(bw["B"], bw["H"], bw["Hkv"], bw["Nq"], bw["Nk"], bw["d"],
                                          dtype="bf16", seed=bw["seed"], device=str(dev))
@@ -141,10 +153,13 @@ def main():
         attn.attn_bwd(bq, bk, bv, bo, bdo, blse, bw["scale"], True, dq=bdq, dk=bdk, dv=bdv,
                       workspace=bws, stream=stream)
         if e: e[3].record(stream)
+        attn.attn_fwd_splitkv(sq, sk, sv, sw["scale"], -1, 0, out=so, lse=slse, workspace=sws,
+                              stream=stream)
+        if e: e[4].record(stream)
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -159,6 +174,8 @@ def main():
     fwd_ms = [ev[0].elapsed_time(ev[1]) for ev in events]
     dec_ms = [ev[1].elapsed_time(ev[2]) for ev in events]
     bwd_ms = [ev[2].elapsed_time(ev[3]) for ev in events]
+    split_ms = [ev[3].elapsed_time(ev[4]) for ev in events]
+    split_avg = sum(split_ms) / len(split_ms)
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     dec_avg = sum(dec_ms) / len(dec_ms)
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
@@ -168,9 +185,11 @@ def main():
     bwd_tflops_fwd_equiv = bwd_flops_fwd_equiv / (bwd_avg * 1e-3) / 1e12
 
     fwd_src = ["exact_tiled_attention_04_amd/csrc/fwd.hip",
-               "exact_tiled_attention_04_amd/csrc/common.hpp"]
+               "exact_tiled_attention_04_amd/csrc/common.hpp",
+               "exact_tiled_attention_04_amd/csrc/kernels.hpp"]
     dec_src = ["exact_tiled_attention_04_amd/csrc/decode.hip",
-               "exact_tiled_attention_04_amd/csrc/common.hpp"]
+               "exact_tiled_attention_04_amd/csrc/common.hpp",
+               "exact_tiled_attention_04_amd/csrc/kernels.hpp"]
     result = {
         "metric": METRIC,
         "value": round(fwd_tflops, 2),
@@ -186,19 +205,20 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "causal_bf16_b1_h32_n8192_d128 (headline) + "
-                        "paged_gqa_decode_bf16_s64_hq32_hkv8_d128 + causal_bwd_bf16_b2_h16_n4096_d128",
+                        "paged_gqa_decode_bf16_s64_hq32_hkv8_d128 + causal_bwd_bf16_b2_h16_n4096_d128"
+                        " + causal_bf16_b1_h4_n8192_d128 (key split)",
             "B": fw["B"], "H": fw["H"], "N": fw["Nq"], "d": fw["d"], "causal": True,
             "plan": attn.attn_plan_describe(attn.ATTN_PHASE_FWD, fw["B"], fw["H"], fw["Hkv"],
                                             fw["Nq"], fw["Nk"], fw["d"], True),
         },
         "roofline": {
-            "kernel": "fwd_bf16_kernel<128,causal,4,32>",
+            "kernel": "fwd_bf16_kernel<D=128,band=causal,NW=4,BC=32>",
             "bound": "mfma",
             "achieved": round(fwd_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": _traffic("fwd_bf16_kernel<128,causal,4,32>", fwd_src, None),
+            "traffic": _traffic("fwd_bf16_kernel<D=128,band=causal,NW=4,BC=32>", fwd_src, None),
             "avg_launch_ms": round(fwd_avg, 4),
             "algorithmic_flop_per_launch": fwd_flops,
         },
@@ -223,8 +243,16 @@ def main():
             "frac_mfma_peak": round(bwd_tflops_algo / PEAK_BF16_TFLOPS, 4),
             "avg_call_ms": round(bwd_avg, 4),
         },
+        "fwd_small_grid": {
+            "workload": "causal_bf16_b1_h4_n8192_d128 (attn_fwd_splitkv)",
+            "value": round(split_flops / (split_avg * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s",
+            "frac_mfma_peak": round(split_flops / (split_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "avg_call_ms": round(split_avg, 4),
+            "workspace_bytes": sws_bytes,
+        },
         "per_call_ms_median": {"fwd": round(med(fwd_ms), 4), "decode": round(med(dec_ms), 4),
-                               "bwd": round(med(bwd_ms), 4)},
+                               "bwd": round(med(bwd_ms), 4), "fwd_small_grid": round(med(split_ms), 4)},
     }
 
     if not args.no_cpu_baseline:

@@ -43,6 +43,57 @@ namespace {
 template <int D>
 constexpr int fwd_bc() { return D == 128 ? 32 : 64; }
 
+// Part `chunk` of a key-tile range t_lo .. t_hi cut into
+// ceil(n / chunk_tiles) parts of equal size (the last may be shorter):
+// narrows the range to that part; false when the part is empty.
+__device__ __forceinline__ bool split_part(int& t_lo, int& t_hi, int chunk_tiles, int chunk) {
+  const int n = t_hi - t_lo + 1;
+  if (n <= 0) return false;
+  const int parts = (n + chunk_tiles - 1) / chunk_tiles;
+  if (chunk >= parts) return false;
+  const int sz = (n + parts - 1) / parts;
+  const int lo = t_lo + chunk * sz;
+  t_hi = min(t_hi, lo + sz - 1);
+  t_lo = lo;
+  return t_lo <= t_hi;
+}
+
+// Query tile and part of key-split unit u.  Units enumerate the (query
+// tile, part) pairs that have work, heaviest (last) query tiles first and
+// each tile's parts in order; the wave finds u's tile by an inclusive scan of
+// the part counts of 64 tiles at a time.
+template <bool BAND>
+__device__ __forceinline__ void split_unit(int u, int n_qtiles, int BR, int Nq, int Nk, int BC,
+                                           int win_left, int win_right, int chunk_tiles,
+                                           int lane, int& qt_out, int& chunk_out) {
+  int qt = 0, chunk = 0;
+  for (int base = 0; base < n_qtiles; base += 64) {
+    const int qr = base + lane;  // position in heavy-first order
+    int parts = 0;
+    if (qr < n_qtiles) {
+      int lo, hi;
+      band_tiles(BAND, (n_qtiles - 1 - qr) * BR, BR, Nq, Nk, BC, win_left, win_right, lo, hi);
+      parts = hi >= lo ? (hi - lo + chunk_tiles) / chunk_tiles : 0;
+    }
+    int incl = parts;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    const unsigned long long hit = __ballot(incl > u);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      qt = n_qtiles - 1 - (base + l);
+      chunk = u - (__shfl(incl, l, 64) - __shfl(parts, l, 64));
+      break;
+    }
+    u -= __shfl(incl, 63, 64);
+  }
+  qt_out = __builtin_amdgcn_readfirstlane(qt);
+  chunk_out = __builtin_amdgcn_readfirstlane(chunk);
+}
+
 // The running maximum is a reference point, not necessarily the exact row
 // maximum: it moves (and the accumulator is rescaled) only when a tile's
 // maximum exceeds it by more than kSlack in base-2 units.  o / l and
@@ -89,10 +140,9 @@ void fwd_bf16_kernel(
   // tile follow each other (each over every head).
   int qt, bh, chunk = 0;
   if (SPLIT) {
-    const int per_qt = n_chunks * BH;
-    qt = n_qtiles - 1 - wg / per_qt;
-    chunk = (wg % per_qt) / BH;
-    bh = (wg % per_qt) % BH;
+    bh = wg % BH;
+    split_unit<BAND>(wg / BH, n_qtiles, BR, Nq, Nk, BC, win_left, win_right, chunk_tiles, lane,
+                     qt, chunk);
   } else {
     qt = n_qtiles - 1 - wg / BH;
     bh = wg % BH;
@@ -120,12 +170,11 @@ void fwd_bf16_kernel(
   band_tiles(BAND, q0, BR, Nq, Nk, BC, win_left, win_right, t_lo, t_hi);
   if (SPLIT) {
     // This workgroup's share of the key range ("Attention kernels",
-    // FlashDecoding paragraph, applied to a prefill query tile): key tiles
-    // chunk * chunk_tiles .. + chunk_tiles - 1.  An empty share exits before
-    // any barrier (the condition is uniform over the workgroup).
-    t_lo = max(t_lo, chunk * chunk_tiles);
-    t_hi = min(t_hi, chunk * chunk_tiles + chunk_tiles - 1);
-    if (t_lo > t_hi) return;
+    // FlashDecoding paragraph, applied to a prefill query tile): the tile's
+    // key tiles cut into equal parts of at most chunk_tiles tiles.  An empty
+    // share exits before any barrier (the condition is uniform over the
+    // workgroup).
+    if (!split_part(t_lo, t_hi, chunk_tiles, chunk)) return;
   }
 
   // Queries of this lane's row as the B operand (Q^T); rows past Nq read 0.
@@ -333,39 +382,45 @@ void fwd_bf16_kernel(
   }
 }
 
-// Merge of one query row's key-split partials (the split-context algebra of
-// "Attention kernels", FlashDecoding paragraph): M = max_c m_c,
+// Merge of the key-split partials of each query row (the split-context
+// algebra of "Attention kernels", FlashDecoding paragraph): M = max_c m_c,
 // w_c = 2^(m_c - M), l = sum_c w_c l_c, O = sum_c w_c o_c / l,
-// LSE = (M + log2 l) ln 2.  One workgroup per (row, batch x head), one thread
-// per output column; the partial loads are issued eight chunks at a time.
+// LSE = (M + log2 l) ln 2.  D/4 threads per row, four columns each (16-byte
+// loads), 256 / (D/4) rows per workgroup; the partial loads are issued eight
+// chunks at a time.
 template <int D>
-__global__ __launch_bounds__(D) void fwd_merge_kernel(
+__global__ __launch_bounds__(256) void fwd_merge_kernel(
     const float* __restrict__ part, __bf16* __restrict__ O, float* __restrict__ LSE, int BH,
     int Nq, int Nk, int n_qtiles, int n_chunks, int chunk_tiles, int band, int win_left,
     int win_right) {
   constexpr int BR = 128;
   constexpr int BC = fwd_bc<D>();
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
   constexpr int kBatch = 8;
-  const int row = blockIdx.x;
   const int bh = blockIdx.y;
-  const int n = threadIdx.x;
+  const int row = blockIdx.x * RPB + (int)threadIdx.x / TPR;
+  const int n4 = ((int)threadIdx.x % TPR) * 4;
+  if (row >= Nq) return;
   const int qt = row / BR;
   int t_lo, t_hi;
   band_tiles(band != 0, qt * BR, BR, Nq, Nk, BC, win_left, win_right, t_lo, t_hi);
-  const int c_lo = t_lo / chunk_tiles;
-  const int c_hi = t_lo <= t_hi ? t_hi / chunk_tiles : c_lo - 1;
+  const int parts = t_lo <= t_hi ? (t_hi - t_lo + chunk_tiles) / chunk_tiles : 0;
   const size_t row0 = ((size_t)bh * n_qtiles + qt) * n_chunks * BR + row % BR;
   const float* ml = part + (size_t)BH * n_qtiles * n_chunks * BR * D;
-  float big_m = -INFINITY, acc = 0.f, ell = 0.f;
-  for (int c0 = c_lo; c0 <= c_hi; c0 += kBatch) {
-    float mv[kBatch], lv[kBatch], ov[kBatch];
+  float big_m = -INFINITY, ell = 0.f;
+  f32x4 acc = f32x4{};
+  for (int c0 = 0; c0 < parts; c0 += kBatch) {
+    float mv[kBatch], lv[kBatch];
+    f32x4 ov[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const bool ok = c0 + j <= c_hi;
-      const size_t prow = row0 + (size_t)(ok ? c0 + j : c_lo) * BR;
+      int lo = t_lo, hi = t_hi;
+      const bool ok = c0 + j < parts && split_part(lo, hi, chunk_tiles, c0 + j);
+      const size_t prow = row0 + (size_t)(ok ? c0 + j : 0) * BR;
       mv[j] = ok ? ml[prow * 2] : -INFINITY;
       lv[j] = ok ? ml[prow * 2 + 1] : 0.f;
-      ov[j] = ok ? part[prow * D + n] : 0.f;
+      ov[j] = ok ? *(const f32x4*)(part + prow * D + n4) : f32x4{};
     }
     float bm = big_m;
 #pragma unroll
@@ -384,8 +439,11 @@ __global__ __launch_bounds__(D) void fwd_merge_kernel(
   }
   const float inv = ell > 0.f ? 1.f / ell : 0.f;
   const size_t orow = (size_t)bh * Nq + row;
-  O[orow * D + n] = (__bf16)(acc * inv);
-  if (n == 0) LSE[orow] = ell > 0.f ? (big_m + fast_log2(ell)) * kLn2 : -INFINITY;
+  u32x2 w;
+  w[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  w[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *(u32x2*)(O + orow * D + n4) = w;
+  if (n4 == 0) LSE[orow] = ell > 0.f ? (big_m + fast_log2(ell)) * kLn2 : -INFINITY;
 }
 
 // fp32 path: the same tiling on v_mfma_f32_32x32x2f32 (P stays fp32).
@@ -553,14 +611,16 @@ hipError_t launch_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
     // workspace for; partials, then the merge.
     const int n_qt = (a.Nq + 127) / 128;
     float* part = (float*)a.workspace;
-    dim3 grid((unsigned)((long long)n_qt * a.n_chunks * a.B * a.H));
+    dim3 grid((unsigned)((long long)a.split_units * a.B * a.H));
     hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 4, BC, true>), grid, dim3(256), 0, stream, q, k, v,
                        o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qt, a.win_left,
                        a.win_right, a.chunk_tiles, a.n_chunks, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fwd_merge_kernel<D>), dim3((unsigned)a.Nq, (unsigned)(a.B * a.H)),
-                       dim3(D), 0, stream, (const float*)part, o, a.LSE, a.B * a.H, a.Nq, a.Nk,
+    constexpr int rpb = 256 / (D / 4);
+    hipLaunchKernelGGL((fwd_merge_kernel<D>),
+                       dim3((unsigned)((a.Nq + rpb - 1) / rpb), (unsigned)(a.B * a.H)), dim3(256), 0,
+                       stream, (const float*)part, o, a.LSE, a.B * a.H, a.Nq, a.Nk,
                        n_qt, a.n_chunks, a.chunk_tiles, a.band, a.win_left, a.win_right);
     return hipGetLastError();
   }

@@ -26,9 +26,11 @@ struct FwdArgs {
   int win_left, win_right;
   bool dtype_bf16;
   // Key split (bf16 path; n_chunks = 0: none): each 128-row query tile's key
-  // tiles are cut into chunks of chunk_tiles tiles, computed as separate
-  // workgroups into `workspace` (fwd_split_workspace_bytes) and merged.
+  // tiles are cut into equal parts of at most chunk_tiles tiles (n_chunks
+  // bounds the part count), computed as separate workgroups into `workspace`
+  // and merged.
   int chunk_tiles, n_chunks;
+  int split_units;     // (query tile, part) pairs with work (the grid / (B*H))
   void* workspace;
 };
 

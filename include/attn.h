@@ -122,8 +122,9 @@ size_t attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int 
  * too few independent programs leaves hardware idle); "Attention kernels",
  * FlashDecoding paragraph (split the keys, merge the partials exactly).
  *   chunk_keys   0: the library splits only when B*H*ceil(Nq/128) < 512 and
- *                chooses the chunk; > 0 (a multiple of 64): always split into
- *                chunks of that many keys (rounded up to whole key tiles).
+ *                chooses the part size; > 0 (a multiple of 64): always split,
+ *                each query tile's key range into equal parts of at most
+ *                that many keys (rounded up to whole key tiles).
  *   workspace    device scratch of attn_fwd_splitkv_workspace_size(...) bytes
  *                (16-byte aligned; may be NULL when that size is 0).
  * The result equals attn_fwd_local's within rounding (the order of the

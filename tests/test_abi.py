@@ -185,7 +185,8 @@ def test_bwd_local_validation(lib, cpu_only):
 
 
 def test_fwd_splitkv_workspace_queries(lib):
-    # Forced 256-key chunks over 1000 keys of d = 128 (32-key tiles): 4 chunks.
+    # Forced 256-key parts over 1000 causal keys of d = 128 (32-key tiles): the
+    # last query tile sees 1000 keys = 32 tiles = 4 parts of 8 tiles.
     assert attn.attn_fwd_splitkv_workspace_size(1, 2, 1000, 1000, 128, -1, 0, 256) == \
         2 * 8 * 4 * 128 * 130 * 4
     assert attn.attn_fwd_splitkv_workspace_size(1, 2, 1000, 1000, 128, -1, 0, 100) == 0
