@@ -18,6 +18,13 @@ probability matrices, so that a reader can check it against the pages by eye:
                        definition with no mask.
 * ``backward``      -- gradients of sum(O * dO) with P recomputed from the
                        definition (textbook softmax Jacobian).
+* ``prefill_ragged`` -- ``forward`` per sequence of a ragged batch in packed
+                       [total, H, d] layout.
+* ``prefill_paged`` -- ragged queries against each sequence's paged context
+                       (gathered as for decode), bottom-right aligned.
+* ``block_sparse_forward`` -- ``forward`` with the pairs restricted to the
+                       score blocks a CSR block index lists
+                       (``block_mask_from_index``).
 * ``brute_force_forward`` -- scalar pure-Python loops, tiny inputs only; a
                        second, structurally different evaluation used to pin
                        ``forward``.
@@ -35,10 +42,14 @@ those values are anchored only by the definition and the pins above
 
 from .attention import (  # noqa: F401
     backward,
+    block_mask_from_index,
+    block_sparse_forward,
     brute_force_backward_dv,
     brute_force_forward,
     decode_paged,
     forward,
     forward_probs,
     gather_paged,
+    prefill_paged,
+    prefill_ragged,
 )

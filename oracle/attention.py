@@ -66,7 +66,7 @@ def _check_shapes(q, k, v):
     return h // hkv
 
 
-def forward_probs(q, k, v, scale, causal, window=None):
+def forward_probs(q, k, v, scale, causal, window=None, mask=None):
     """Materialised attention: returns (O, LSE, P).
 
     [MAK] "Standard attention materializes quadratic state":
@@ -79,6 +79,9 @@ def forward_probs(q, k, v, scale, causal, window=None):
 
     q: [B, H, Nq, d]; k, v: [B, Hkv, Nk, d] (any float dtype, computed in fp64).
     window: optional (left, right) local-attention band, see ``_visible``.
+    mask: optional boolean array broadcastable to [B, H, Nq, Nk]; True keeps
+    the pair.  It is intersected with the causal/window visibility (an
+    arbitrary sparse mask, [MAK] "Kernel structure").
     Returns O [B, H, Nq, d], LSE [B, H, Nq], P [B, H, Nq, Nk], all float64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -87,7 +90,9 @@ def forward_probs(q, k, v, scale, causal, window=None):
     group = _check_shapes(q, k, v)
     bsz, nh, nq, d = q.shape
     nk = k.shape[2]
-    vis = _visible(nq, nk, causal, window)
+    vis_all = np.broadcast_to(_visible(nq, nk, causal, window), (bsz, nh, nq, nk))
+    if mask is not None:
+        vis_all = vis_all & np.broadcast_to(np.asarray(mask, dtype=bool), (bsz, nh, nq, nk))
 
     out = np.zeros((bsz, nh, nq, d))
     lse = np.full((bsz, nh, nq), -np.inf)
@@ -96,7 +101,7 @@ def forward_probs(q, k, v, scale, causal, window=None):
         for h in range(nh):
             g = h // group
             s = scale * (q[b, h] @ k[b, g].T)
-            s = np.where(vis, s, -np.inf)
+            s = np.where(vis_all[b, h], s, -np.inf)
             m = s.max(axis=1) if nk > 0 else np.full(nq, -np.inf)
             live = np.isfinite(m)
             e = np.zeros_like(s)
@@ -110,9 +115,12 @@ def forward_probs(q, k, v, scale, causal, window=None):
     return out, lse, probs
 
 
-def forward(q, k, v, scale, causal, window=None):
+def forward(q, k, v, scale, causal, window=None, mask=None):
     """(O, LSE) of :func:`forward_probs`."""
-    out, lse, _ = forward_probs(q, k, v, scale, causal, window)
+    if mask is None:
+        out, lse, _ = forward_probs(q, k, v, scale, causal, window)
+    else:
+        out, lse, _ = forward_probs(q, k, v, scale, causal, window, mask=mask)
     return out, lse
 
 
@@ -210,12 +218,127 @@ def decode_paged(q, k_cache, v_cache, block_table, context_lens, scale):
     return out, lse
 
 
-def brute_force_forward(q, k, v, scale, causal, window=None):
+def prefill_ragged(q, k, v, cu_q, cu_k, scale, causal, window=None):
+    """Forward over a ragged batch of sequences in packed layout.
+
+    [MAK] "Numerical validation" lists ragged sequence boundaries among the
+    cases a fused kernel must get right; a serving engine ("Paged attention
+    changes addressing", last paragraph) runs tiled prefill over many
+    sequences of different lengths at once.  Each sequence is an independent
+    attention problem: sequence s owns query rows cu_q[s] .. cu_q[s+1] - 1 and
+    key rows cu_k[s] .. cu_k[s+1] - 1, and this is ``forward`` applied to each
+    slice (bottom-right causal alignment within the sequence).
+
+    q: [total_q, H, d]; k, v: [total_k, Hkv, d]; cu_q, cu_k: [num_seqs + 1]
+    non-decreasing offsets starting at 0.
+    Returns O [total_q, H, d] and LSE [H, total_q], float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    total_q, nh, d = q.shape
+    out = np.zeros((total_q, nh, d))
+    lse = np.full((nh, total_q), -np.inf)
+    for s in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[s], cu_q[s + 1], cu_k[s], cu_k[s + 1]
+        if q1 <= q0:
+            continue
+        qs = q[q0:q1].transpose(1, 0, 2)[None]
+        ks = k[k0:k1].transpose(1, 0, 2)[None]
+        vs = v[k0:k1].transpose(1, 0, 2)[None]
+        o, l_ = forward(qs, ks, vs, scale, causal, window)
+        out[q0:q1] = o[0].transpose(1, 0, 2)
+        lse[:, q0:q1] = l_[0]
+    return out, lse
+
+
+def prefill_paged(q, k_cache, v_cache, block_table, cu_q, seqlens_k, scale, causal,
+                  window=None):
+    """Ragged prefill whose keys and values live in a paged cache.
+
+    The combination a serving engine runs ([MAK] "Paged attention changes
+    addressing", last paragraph): sequence s has seqlens_k[s] tokens in the
+    cache, gathered through its block table exactly as for decode, and its
+    cu_q[s+1] - cu_q[s] query rows are the LAST positions of that context
+    (a prefill chunk whose keys were already appended), bottom-right aligned.
+    With one query row this is ``decode_paged``; with as many rows as
+    tokens it is a full prefill.
+
+    q: [total_q, Hq, d]; caches [num_blocks, block_size, Hkv, d]; block_table
+    [num_seqs, max_blocks]; cu_q [num_seqs + 1]; seqlens_k [num_seqs].
+    Returns O [total_q, Hq, d] and LSE [Hq, total_q], float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    cu_q = [int(x) for x in cu_q]
+    total_q, nh, d = q.shape
+    out = np.zeros((total_q, nh, d))
+    lse = np.full((nh, total_q), -np.inf)
+    for s in range(len(cu_q) - 1):
+        q0, q1 = cu_q[s], cu_q[s + 1]
+        ctx = max(int(seqlens_k[s]), 0)
+        if q1 <= q0:
+            continue
+        ks = gather_paged(k_cache, block_table, s, ctx).astype(np.float64)
+        vs = gather_paged(v_cache, block_table, s, ctx).astype(np.float64)
+        qs = q[q0:q1].transpose(1, 0, 2)[None]
+        o, l_ = forward(qs, ks.transpose(1, 0, 2)[None], vs.transpose(1, 0, 2)[None], scale,
+                        causal, window)
+        out[q0:q1] = o[0].transpose(1, 0, 2)
+        lse[:, q0:q1] = l_[0]
+    return out, lse
+
+
+def block_mask_from_index(row_ptr, col_idx, n_qblocks, n_kblocks):
+    """Dense boolean [L, n_qblocks, n_kblocks] block matrix of a CSR block index.
+
+    [MAK] "Kernel structure": an arbitrary sparse mask needs an index
+    structure that tells the kernel which blocks exist.  Here layout l lists,
+    for query block r, the key blocks col_idx[row_ptr[l, r] : row_ptr[l, r+1]].
+    row_ptr: [L, n_qblocks + 1] offsets into col_idx (int).
+    """
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    col_idx = np.asarray(col_idx, dtype=np.int64)
+    n_layouts = row_ptr.shape[0]
+    blocks = np.zeros((n_layouts, n_qblocks, n_kblocks), dtype=bool)
+    for lay in range(n_layouts):
+        for r in range(n_qblocks):
+            for c in col_idx[row_ptr[lay, r]:row_ptr[lay, r + 1]]:
+                blocks[lay, r, c] = True
+    return blocks
+
+
+def block_sparse_forward(q, k, v, scale, causal, blocks, block_q, block_k):
+    """Attention restricted to the listed score blocks ([MAK] "Kernel
+    structure", sparse masks; "Paged attention changes addressing": sparse
+    attention visits selected score blocks).
+
+    blocks: boolean [L, ceil(Nq / block_q), ceil(Nk / block_k)]; (batch b,
+    head h) uses layout (b * H + h) % L.  Query row i may see key j iff block
+    (i // block_q, j // block_k) is listed, intersected with the causal mask
+    when ``causal``.  This is ``forward`` with that boolean mask.
+    """
+    blocks = np.asarray(blocks, dtype=bool)
+    bsz, nh, nq, _ = np.shape(q)
+    nk = np.shape(k)[2]
+    n_layouts = blocks.shape[0]
+    rows = np.arange(nq) // block_q
+    cols = np.arange(nk) // block_k
+    mask = np.zeros((bsz, nh, nq, nk), dtype=bool)
+    for b in range(bsz):
+        for h in range(nh):
+            mask[b, h] = blocks[(b * nh + h) % n_layouts][rows[:, None], cols[None, :]]
+    return forward(q, k, v, scale, causal, mask=mask)
+
+
+def brute_force_forward(q, k, v, scale, causal, window=None, allowed=None):
     """Scalar pure-Python attention for tiny inputs (N <= 8, d <= 8).
 
     A second evaluation of the same definition with no numpy arithmetic:
     nested loops, math.exp, and a max taken over the visible keys only (the
     visibility test written out again, not shared with ``_visible``).
+    ``allowed(b, h, i, j)``, if given, is an extra predicate a pair must pass.
     Inputs are nested lists or arrays; returns nested lists O, LSE.
     """
     left, right = window if window is not None else (None, None)
@@ -240,6 +363,8 @@ def brute_force_forward(q, k, v, scale, causal, window=None):
                     if left is not None and j < pos - left:
                         continue
                     if right is not None and j > pos + right:
+                        continue
+                    if allowed is not None and not allowed(b, h, i, j):
                         continue
                     dot = 0.0
                     for c in range(d):
