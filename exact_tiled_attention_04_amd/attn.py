@@ -8,9 +8,10 @@ been built (``python -m exact_tiled_attention_04_amd.build``) the first call
 raises.
 
 Names follow the C ABI: ``attn_fwd``, ``attn_fwd_local``, ``attn_fwd_splitkv``,
-``attn_fwd_splitkv_workspace_size``, ``attn_decode_paged``,
-``attn_bwd``, ``attn_bwd_local``, ``attn_decode_paged_workspace_size``,
-``attn_bwd_workspace_size``, ``attn_plan_describe``, ``attn_status_string``.
+``attn_fwd_splitkv_workspace_size``, ``attn_fwd_varlen``, ``attn_prefill_paged``,
+``attn_fwd_block_sparse``, ``attn_decode_paged``, ``attn_bwd``, ``attn_bwd_local``,
+``attn_decode_paged_workspace_size``, ``attn_bwd_workspace_size``,
+``attn_plan_describe``, ``attn_status_string``.
 """
 
 import ctypes
@@ -38,6 +39,9 @@ EXPORTED = (
     "attn_fwd_local",
     "attn_fwd_splitkv_workspace_size",
     "attn_fwd_splitkv",
+    "attn_fwd_varlen",
+    "attn_prefill_paged",
+    "attn_fwd_block_sparse",
     "attn_bwd_local",
     "attn_decode_paged_workspace_size",
     "attn_decode_paged",
@@ -81,6 +85,15 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
                                      i32, i32, i32, vp, sz, vp]
     lib.attn_fwd_splitkv.restype = i32
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    f32, i32, i32, i32, vp]
+    lib.attn_fwd_varlen.restype = i32
+    lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                       i32, i32, i32, i64, i64, i64, f32, i32, i32, i32, vp]
+    lib.attn_prefill_paged.restype = i32
+    lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                          i32, vp, vp, i32, i32, i32, vp]
+    lib.attn_fwd_block_sparse.restype = i32
     lib.attn_decode_paged_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_decode_paged_workspace_size.restype = sz
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -202,6 +215,87 @@ def attn_fwd_splitkv(q, k, v, scale, window_left=-1, window_right=-1, chunk_keys
                                 float(scale), int(window_left), int(window_right),
                                 _dtype_code(q), int(chunk_keys), _ptr(workspace),
                                 0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def _need_int32(*ts):
+    for t in ts:
+        if t.dtype != torch.int32:
+            raise TypeError("offset, length and index tensors must be int32")
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale, window_left=-1,
+                    window_right=-1, out=None, lse=None, stream=None):
+    """Ragged batch in packed layout: q [total_q, H, d]; k, v [total_k, Hkv, d];
+    cu_seqlens_q/k int32 [num_seqs + 1] on the device.  Returns O [total_q, H, d]
+    and LSE [H, total_q].  (-1, 0) windows give the causal mask."""
+    lib = load_library()
+    _need_device(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    _need_int32(cu_seqlens_q, cu_seqlens_k)
+    total_q, H, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    if k.shape != (total_k, Hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [total_k, Hkv, d]")
+    num_seqs = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != num_seqs + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have num_seqs + 1 entries")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need_device(out, lse)
+    _check(lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                               _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, total_q, total_k,
+                               int(max_seqlen_q), H, Hkv, d, float(scale), int(window_left),
+                               int(window_right), _dtype_code(q), _stream(stream)))
+    return out, lse
+
+
+def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, max_seqlen_q,
+                       scale, window_left=-1, window_right=-1, num_blocks=None, strides=None,
+                       out=None, lse=None, stream=None):
+    """Ragged queries q [total_q, Hq, d] against a paged cache
+    [num_blocks, block_size, Hkv, d] (or ``strides`` = (block, token, head) in
+    elements); block_table int32 [num_seqs, max_blocks]; cu_seqlens_q int32
+    [num_seqs + 1]; seqlens_k int32 [num_seqs].  Each sequence's queries are
+    the last positions of its cached context.  Returns O and LSE [Hq, total_q]."""
+    lib = load_library()
+    _need_device(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k)
+    _need_int32(block_table, cu_seqlens_q, seqlens_k)
+    total_q, Hq, d = q.shape
+    nb, block_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    num_blocks = nb if num_blocks is None else num_blocks
+    num_seqs = cu_seqlens_q.numel() - 1
+    if seqlens_k.numel() != num_seqs or block_table.shape[0] != num_seqs:
+        raise ValueError("seqlens_k and block_table must have num_seqs rows")
+    if strides is None:
+        strides = (block_size * Hkv * d, Hkv * d, d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need_device(out, lse)
+    _check(lib.attn_prefill_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cu_seqlens_q),
+        _ptr(seqlens_k), _ptr(out), _ptr(lse), num_seqs, total_q, int(max_seqlen_q), Hq, Hkv, d,
+        block_size, int(num_blocks), block_table.shape[1], int(strides[0]), int(strides[1]),
+        int(strides[2]), float(scale), int(window_left), int(window_right), _dtype_code(q),
+        _stream(stream)))
+    return out, lse
+
+
+def attn_fwd_block_sparse(q, k, v, scale, causal, row_ptr, col_idx, out=None, lse=None,
+                          stream=None):
+    """attn_fwd restricted to the listed 128x128 score blocks: row_ptr int32
+    [num_layouts, ceil(Nq/128) + 1], col_idx int32 [nnz] (device); (b, h) uses
+    layout (b*H + h) % num_layouts."""
+    lib = load_library()
+    dims, out, lse = _fwd_args(q, k, v, out, lse)
+    _need_device(row_ptr, col_idx)
+    _need_int32(row_ptr, col_idx)
+    B, H, _, Nq, _, _ = dims
+    if row_ptr.dim() != 2 or row_ptr.shape[1] != (Nq + 127) // 128 + 1:
+        raise ValueError("row_ptr must be [num_layouts, ceil(Nq/128) + 1]")
+    _check(lib.attn_fwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *dims,
+                                     float(scale), int(bool(causal)), _ptr(row_ptr),
+                                     _ptr(col_idx), row_ptr.shape[0], col_idx.numel(),
+                                     _dtype_code(q), _stream(stream)))
     return out, lse
 
 

@@ -251,9 +251,157 @@ attn_status_t bwd_impl(const void* Q, const void* K, const void* V, const void* 
   return ok();
 }
 
+// Checks shared by the packed (ragged and paged) forward entry points.
+attn_status_t check_packed(const void* Q, const void* O, const float* LSE, const int32_t* cu_q,
+                           int num_seqs, int total_q, int max_seqlen_q, int H, int Hkv, int d,
+                           float scale, attn_dtype_t dtype) {
+  if (!Q || !O || !LSE || !cu_q) return fail(ATTN_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(Q) || !aligned16(O) || ((uintptr_t)LSE & 3u) || ((uintptr_t)cu_q & 3u))
+    return fail(ATTN_ERR_INVALID_ARG, "misaligned pointer argument");
+  if (num_seqs < 1 || total_q < 1 || max_seqlen_q < 1 || max_seqlen_q > total_q || H < 1 ||
+      Hkv < 1)
+    return fail(ATTN_ERR_INVALID_ARG,
+                "bad sizes (num_seqs=%d total_q=%d max_seqlen_q=%d H=%d Hkv=%d)", num_seqs,
+                total_q, max_seqlen_q, H, Hkv);
+  if (H % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+  if (dtype != ATTN_DTYPE_BF16) {
+    if (dtype != ATTN_DTYPE_F32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    return fail(ATTN_ERR_UNSUPPORTED, "packed and paged forward support bf16 only");
+  }
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(ATTN_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension %d not in {64,128}", d);
+  // Packed rows are addressed with 32-bit byte offsets from a sequence's first row.
+  if ((long long)total_q * H * d * 2 >= (1LL << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "packed queries exceed 2 GiB");
+  if ((long long)((max_seqlen_q + 127) / 128) * num_seqs * H > kMaxGrid)
+    return fail(ATTN_ERR_INVALID_ARG, "grid too large");
+  return ATTN_OK;
+}
+
+attn_status_t launch_mode(eta::FwdArgs& a, void* stream) {
+  eta::FwdPlan p{};
+  hipError_t e = eta::launch_fwd(a, p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+attn_status_t attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int num_seqs, int total_q, int total_k, int max_seqlen_q, int H,
+                              int Hkv, int d, float scale, int window_left, int window_right,
+                              attn_dtype_t dtype, void* stream) {
+  int left, right;
+  if (!window_sides(window_left, window_right, &left, &right))
+    return fail(ATTN_ERR_INVALID_ARG, "window sides must be >= -1 (got %d, %d)", window_left,
+                window_right);
+  attn_status_t st = check_packed(Q, O, LSE, cu_seqlens_q, num_seqs, total_q, max_seqlen_q, H,
+                                  Hkv, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (!K || !V || !cu_seqlens_k) return fail(ATTN_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(K) || !aligned16(V) || ((uintptr_t)cu_seqlens_k & 3u))
+    return fail(ATTN_ERR_INVALID_ARG, "misaligned pointer argument");
+  if (total_k < 0) return fail(ATTN_ERR_INVALID_ARG, "total_k=%d must be >= 0", total_k);
+  if ((long long)total_k * Hkv * d * 2 >= (1LL << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "packed keys exceed 2 GiB");
+  const bool band = left != eta::kUnbounded || right != eta::kUnbounded;
+  eta::FwdArgs a{Q, K, V, O, LSE, num_seqs, H, Hkv, max_seqlen_q, 0, d, scale, 0, band ? 1 : 0,
+                 left, right, true, 0, 0, 0, nullptr, eta::kFwdRagged, eta::FwdSeqArgs{}};
+  a.seq.cu_q = cu_seqlens_q;
+  a.seq.k_lens = cu_seqlens_k;
+  a.seq.total_q = total_q;
+  a.seq.total_k = total_k;
+  return launch_mode(a, stream);
+}
+
+attn_status_t attn_prefill_paged(const void* Q, const void* K_cache, const void* V_cache,
+                                 const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                 const int32_t* seqlens_k, void* O, float* LSE, int num_seqs,
+                                 int total_q, int max_seqlen_q, int Hq, int Hkv, int d,
+                                 int block_size, int num_blocks, int max_blocks_per_seq,
+                                 int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                                 float scale, int window_left, int window_right,
+                                 attn_dtype_t dtype, void* stream) {
+  int left, right;
+  if (!window_sides(window_left, window_right, &left, &right))
+    return fail(ATTN_ERR_INVALID_ARG, "window sides must be >= -1 (got %d, %d)", window_left,
+                window_right);
+  attn_status_t st = check_packed(Q, O, LSE, cu_seqlens_q, num_seqs, total_q, max_seqlen_q, Hq,
+                                  Hkv, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (!K_cache || !V_cache || !block_table || !seqlens_k)
+    return fail(ATTN_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(K_cache) || !aligned16(V_cache) || ((uintptr_t)block_table & 3u) ||
+      ((uintptr_t)seqlens_k & 3u))
+    return fail(ATTN_ERR_INVALID_ARG, "misaligned pointer argument");
+  if (block_size < 1 || num_blocks < 1 || max_blocks_per_seq < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "bad cache sizes (block_size=%d num_blocks=%d "
+                "max_blocks_per_seq=%d)", block_size, num_blocks, max_blocks_per_seq);
+  // Each wave's 8 (d = 128) or 16 (d = 64) rows of a key tile must share a page.
+  if (block_size % 16 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "paged prefill needs block_size %% 16 == 0 (got %d)",
+                block_size);
+  if ((long long)max_blocks_per_seq * block_size >= (1LL << 31))
+    return fail(ATTN_ERR_INVALID_ARG, "block table capacity exceeds 2^31 tokens");
+  if (head_stride < d || token_stride < (int64_t)Hkv * head_stride ||
+      block_stride < (int64_t)block_size * token_stride || head_stride % 8 || token_stride % 8 ||
+      block_stride % 8)
+    return fail(ATTN_ERR_INVALID_ARG,
+                "cache strides inconsistent with block_size=%d Hkv=%d d=%d "
+                "(block=%lld token=%lld head=%lld)",
+                block_size, Hkv, d, (long long)block_stride, (long long)token_stride,
+                (long long)head_stride);
+  if (token_stride >= (1LL << 24))
+    return fail(ATTN_ERR_UNSUPPORTED, "token_stride=%lld elements exceeds 2^24",
+                (long long)token_stride);
+  const bool band = left != eta::kUnbounded || right != eta::kUnbounded;
+  eta::FwdArgs a{Q, K_cache, V_cache, O, LSE, num_seqs, Hq, Hkv, max_seqlen_q, 0, d, scale, 0,
+                 band ? 1 : 0, left, right, true, 0, 0, 0, nullptr, eta::kFwdPaged,
+                 eta::FwdSeqArgs{}};
+  a.seq.cu_q = cu_seqlens_q;
+  a.seq.k_lens = seqlens_k;
+  a.seq.block_table = block_table;
+  a.seq.total_q = total_q;
+  a.seq.max_blocks = max_blocks_per_seq;
+  a.seq.num_blocks = num_blocks;
+  a.seq.block_size = block_size;
+  a.seq.block_stride = block_stride;
+  a.seq.token_stride = token_stride;
+  a.seq.head_stride = head_stride;
+  return launch_mode(a, stream);
+}
+
+attn_status_t attn_fwd_block_sparse(const void* Q, const void* K, const void* V, void* O,
+                                    float* LSE, int B, int H, int Hkv, int Nq, int Nk, int d,
+                                    float scale, int causal, const int32_t* row_ptr,
+                                    const int32_t* col_idx, int num_layouts, int nnz,
+                                    attn_dtype_t dtype, void* stream) {
+  if (!Q || !K || !V || !O || !LSE || !row_ptr || !col_idx)
+    return fail(ATTN_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE) ||
+      ((uintptr_t)row_ptr & 3u) || ((uintptr_t)col_idx & 3u))
+    return fail(ATTN_ERR_INVALID_ARG, "misaligned pointer argument");
+  attn_status_t st = check_fwd_shape(B, H, Hkv, Nq, Nk, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_DTYPE_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "block-sparse forward supports bf16 only");
+  if (num_layouts < 1) return fail(ATTN_ERR_INVALID_ARG, "num_layouts=%d must be >= 1", num_layouts);
+  if (nnz < 0) return fail(ATTN_ERR_INVALID_ARG, "nnz=%d must be >= 0", nnz);
+  if ((long long)B * H * ((Nq + 127) / 128) > kMaxGrid)
+    return fail(ATTN_ERR_INVALID_ARG, "grid too large");
+  eta::FwdArgs a{Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, causal ? 1 : 0, causal ? 1 : 0,
+                 eta::kUnbounded, causal ? 0 : eta::kUnbounded, true, 0, 0, 0, nullptr,
+                 eta::kFwdSparse, eta::FwdSeqArgs{}};
+  a.seq.row_ptr = row_ptr;
+  a.seq.col_idx = col_idx;
+  a.seq.num_layouts = num_layouts;
+  a.seq.nnz = nnz;
+  return launch_mode(a, stream);
+}
 
 
 attn_status_t attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,

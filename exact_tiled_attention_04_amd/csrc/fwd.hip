@@ -102,13 +102,26 @@ __device__ __forceinline__ void split_unit(int u, int n_qtiles, int BR, int Nq, 
 constexpr float kSlack = 8.f;
 
 
-template <int D, bool BAND, int NW, int BC, bool SPLIT>
+// Where a workgroup's rows live and which key tiles it visits.
+//   kFwdDense:  Q, O [B, H, N, d]; K, V [B, Hkv, N, d]; a contiguous tile range.
+//   kFwdRagged: packed sequences ("Numerical validation": ragged sequence
+//            boundaries): Q, O [total_q, H, d], K, V [total_k, Hkv, d];
+//            sequence s owns rows cu_q[s] .. cu_q[s+1] - 1 and
+//            cu_k[s] .. cu_k[s+1] - 1.
+//   kFwdPaged:  packed ragged queries over a paged K/V cache ("Paged attention
+//            changes addressing": a token's page comes from the sequence's
+//            block table); sequence s has seqlens_k[s] cached tokens.
+//   kFwdSparse: dense rows, but the workgroup visits only the 128-key blocks a
+//            CSR block index lists for its 128-row query block ("Kernel
+//            structure": sparse masks need an index of the blocks that exist).
+
+template <int D, bool BAND, int NW, int BC, bool SPLIT, int MODE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BC == 32 ? 3 : 2)))
 void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
     int B, int H, int Hkv, int Nq, int Nk, float scale_log2, int n_qtiles, int win_left,
-    int win_right, int chunk_tiles, int n_chunks, float* __restrict__ part) {
+    int win_right, int chunk_tiles, int n_chunks, float* __restrict__ part, FwdSeqArgs sq) {
   constexpr int NT = NW * 64;
   constexpr int BR = NW * 32;
   constexpr int CH = D / 8;                  // 16-byte chunks per row
@@ -118,13 +131,24 @@ void fwd_bf16_kernel(
   constexpr int ROW = D * 2;                 // bytes per row
   constexpr int TILE = BC * ROW;            // bytes per K (or V) tile
   constexpr int KB = BC / 32;                // 32-key blocks per tile
+  constexpr int RPI = 64 / CH;               // tile rows per copy instruction
+  constexpr int WROWS = NLOAD * RPI;         // tile rows copied by one wave
+  constexpr int TPB = 128 / BC;              // key tiles per 128-key sparse block
+  constexpr bool PACKED = MODE == kFwdRagged || MODE == kFwdPaged;
   static_assert(BC * CH % NT == 0, "tile load split");
   static_assert(BC == 32 || BC == 64, "tile width");
+  static_assert(!(SPLIT && MODE != kFwdDense), "key split on dense rows only");
+  static_assert(MODE == kFwdDense || NW == 4, "128-row query tiles");
 
   // Two LDS buffers (K tile then V tile each) as separate objects, so the
   // direct copies into one are known not to alias reads of the other.
   __shared__ __attribute__((aligned(16))) char smem0[2 * TILE];
   __shared__ __attribute__((aligned(16))) char smem1[2 * TILE];
+  // Paged: per buffer, one flag per wave marking its rows of the tile as
+  // coming from a page outside the cache (those keys are masked).
+  constexpr int NBAD = MODE == kFwdPaged ? NW : 1;
+  __shared__ int bad0[NBAD];
+  __shared__ int bad1[NBAD];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -147,17 +171,45 @@ void fwd_bf16_kernel(
     qt = n_qtiles - 1 - wg / BH;
     bh = wg % BH;
   }
-  const int b = bh / H;
+  const int b = bh / H;       // batch, or sequence of a packed batch
   const int h = bh % H;
   const int g = h / (H / Hkv);
   const int q0 = qt * BR;
+
+  // Rows of this (batch or sequence, head): element offsets of the first
+  // query and key row, and byte strides between rows.  Offsets of packed
+  // sequences are clamped into the packed tensors, so inconsistent offsets
+  // cannot move an access outside them.
+  size_t q_elem, k_elem = 0;
+  int q_begin = 0;
+  if constexpr (PACKED) {
+    q_begin = min(max(sq.cu_q[b], 0), sq.total_q);
+    const int q_end = min(max(sq.cu_q[b + 1], q_begin), sq.total_q);
+    Nq = q_end - q_begin;
+    if (q0 >= Nq) return;  // uniform over the workgroup, before any barrier
+    if constexpr (MODE == kFwdRagged) {
+      const int k_begin = min(max(sq.k_lens[b], 0), sq.total_k);
+      Nk = min(max(sq.k_lens[b + 1], k_begin), sq.total_k) - k_begin;
+      k_elem = ((size_t)k_begin * Hkv + g) * D;
+    } else {
+      Nk = min(max(sq.k_lens[b], 0), sq.max_blocks * sq.block_size);
+    }
+    q_elem = ((size_t)q_begin * H + h) * D;
+  } else {
+    q_elem = ((size_t)b * H + h) * (size_t)Nq * D;
+    k_elem = ((size_t)b * Hkv + g) * (size_t)Nk * D;
+  }
+  constexpr int QS = PACKED ? 0 : ROW;  // query row stride when known at compile time
+  const int qstride = PACKED ? H * ROW : QS;
+  const int kstride = MODE == kFwdRagged ? Hkv * ROW : ROW;
   const int off = Nk - Nq;  // bottom-right causal alignment
 
-  const buf_rsrc qrs = make_rsrc(Q + ((size_t)b * H + h) * (size_t)Nq * D, (unsigned)Nq * ROW);
-  const buf_rsrc krs = make_rsrc(K + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
-  const buf_rsrc vrs = make_rsrc(V + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
-  __bf16* Op = O + ((size_t)b * H + h) * (size_t)Nq * D;
-  float* Lp = LSE + ((size_t)b * H + h) * (size_t)Nq;
+  const buf_rsrc qrs = make_rsrc(Q + q_elem, (unsigned)Nq * (unsigned)qstride);
+  const buf_rsrc krs = make_rsrc(K + k_elem, MODE == kFwdPaged ? 0u : (unsigned)Nk * (unsigned)kstride);
+  const buf_rsrc vrs = make_rsrc(V + k_elem, MODE == kFwdPaged ? 0u : (unsigned)Nk * (unsigned)kstride);
+  __bf16* Op = O + q_elem;
+  float* Lp = PACKED ? LSE + (size_t)h * sq.total_q + q_begin
+                     : LSE + ((size_t)b * H + h) * (size_t)Nq;
 
   const int qrow = q0 + wave * 32 + li;
   const int wave_row_lo = q0 + wave * 32;
@@ -177,22 +229,56 @@ void fwd_bf16_kernel(
     if (!split_part(t_lo, t_hi, chunk_tiles, chunk)) return;
   }
 
+  // The visited tiles as a sequence j = 0 .. n_iter - 1: the range t_lo ..
+  // t_hi, or (sparse) the listed blocks' tiles in list order.  A listed block
+  // outside the key range maps to -2: the step copies and computes nothing.
+  int n_iter = t_hi - t_lo + 1;
+  int sp_lo = 0, sp_base = 0, sp_cols = 0, n_kblk = 0;
+  if constexpr (MODE == kFwdSparse) {
+    const int lay = bh % sq.num_layouts;
+    const int* rp = sq.row_ptr + (size_t)lay * (n_qtiles + 1);
+    // Offsets are clamped into col_idx's nnz entries.
+    sp_lo = min(max(rp[qt], 0), sq.nnz);
+    const int cnt = min(max(rp[qt + 1], sp_lo), sq.nnz) - sp_lo;
+    n_iter = cnt * TPB;
+    n_kblk = (Nk + 127) / 128;
+    sp_cols = lane < cnt ? sq.col_idx[sp_lo + lane] : -1;
+  }
+  auto tile_at = [&](int j) -> int {
+    if constexpr (MODE == kFwdSparse) {
+      const int bi = j / TPB;
+      if (bi - sp_base >= 64) {  // next 64 entries of the row's list
+        sp_base = bi & ~63;
+        const int cnt = n_iter / TPB;
+        sp_cols = sp_base + lane < cnt ? sq.col_idx[sp_lo + sp_base + lane] : -1;
+      }
+      const int blk = __builtin_amdgcn_readlane(sp_cols, bi - sp_base);
+      const int t = blk * TPB + j % TPB;
+      return (blk >= 0 && blk < n_kblk && t >= t_lo && t <= t_hi) ? t : -2;
+    } else {
+      return t_lo + j;
+    }
+  };
+
   // Queries of this lane's row as the B operand (Q^T); rows past Nq read 0.
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(qrs, qrow * ROW + (16 * ks + 8 * hh) * 2, 0));
+    qf[ks] = __builtin_bit_cast(bf16x8,
+                                buf_load16(qrs, qrow * (QS ? QS : qstride) + (16 * ks + 8 * hh) * 2, 0));
 
   // Direct copies: instruction `it` of this wave fills 16-byte LDS slots
   // p = (wave * NLOAD + it) * 64 + lane of a tile, i.e. row p / CH and
-  // swizzled chunk p % CH; the lane loads the logical chunk that belongs there.
+  // swizzled chunk p % CH; the lane loads the logical chunk that belongs there
+  // (paged: relative to the wave's first row, whose page holds all WROWS rows).
   int goff[NLOAD];
 #pragma unroll
   for (int it = 0; it < NLOAD; ++it) {
     const int p = (wave * NLOAD + it) * 64 + lane;
     const int row = p / CH;
     const int c = (p % CH) ^ tile_swz<D>(row);
-    goff[it] = row * ROW + c * 16;
+    goff[it] = MODE == kFwdPaged ? (row - wave * WROWS) * (int)(sq.token_stride * 2) + c * 16
+                              : row * kstride + c * 16;
   }
   int kofs[KS];   // K row (32 kb + li), chunk 2 ks + hh
 #pragma unroll
@@ -213,22 +299,78 @@ void fwd_bf16_kernel(
   float m_run = -INFINITY;  // reference max, base-2 units (scores * scale * log2 e)
   float l_run = 0.f;        // this lane's partial running sum
 
-  auto load_tile = [&](int t, char* dst) {
-    const int soff = t * TILE;  // rows past Nk arrive as zeros (buffer range)
-#pragma unroll
-    for (int it = 0; it < NLOAD; ++it) {
-      char* slot = dst + (wave * NLOAD + it) * 1024;
-      buf_load16_lds(krs, slot, goff[it], soff);
-      buf_load16_lds(vrs, slot + TILE, goff[it], soff);
+  // Paged: the physical page of this wave's rows of tile t (wave-uniform; a
+  // scalar load issued one step before the copy that needs it).
+  auto page_of = [&](int t) -> int {
+    if constexpr (MODE == kFwdPaged) {
+      if (t < 0) return -1;
+      const int key = t * BC + wave * WROWS;
+      if (key >= Nk) return -1;
+      return sq.block_table[(size_t)b * sq.max_blocks + key / sq.block_size];
+    } else {
+      return 0;
     }
   };
 
-  auto step = [&](int t, const char* Ks, char* next) {
+  auto load_tile = [&](int t, char* dst, int* bad_dst, int phys) {
+    if constexpr (MODE == kFwdPaged) {
+      // A buffer resource over this wave's rows in their page: its range
+      // ends after the last live token, and is empty for a page outside the
+      // cache, so such rows arrive as zeros ("Failure modes": a page-table
+      // mismatch must not read outside the cache) and are flagged so that
+      // their keys get probability 0.
+      const int key = t * BC + wave * WROWS;
+      int live = min(max(Nk - key, 0), WROWS);
+      const bool bad = live > 0 && (phys < 0 || phys >= sq.num_blocks);
+      if (bad) live = 0;
+      if (lane == 0) bad_dst[wave] = bad ? 1 : 0;
+      unsigned long long eo = live ? (unsigned long long)phys * sq.block_stride +
+                                         (unsigned long long)(key % sq.block_size) * sq.token_stride +
+                                         (unsigned long long)g * sq.head_stride
+                                   : 0;
+      // All of it is wave-uniform; readfirstlane lets the compiler keep the
+      // resources in SGPRs (no per-lane loop around the copies).
+      live = __builtin_amdgcn_readfirstlane(live);
+      const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)eo);
+      const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(eo >> 32));
+      eo = ((unsigned long long)hi << 32) | lo;
+      const unsigned bytes = (unsigned)live * (unsigned)(sq.token_stride * 2);
+      const buf_rsrc kp = make_rsrc(K + eo, bytes);
+      const buf_rsrc vp = make_rsrc(V + eo, bytes);
+#pragma unroll
+      for (int it = 0; it < NLOAD; ++it) {
+        char* slot = dst + (wave * NLOAD + it) * 1024;
+        buf_load16_lds(kp, slot, goff[it], 0);
+        buf_load16_lds(vp, slot + TILE, goff[it], 0);
+      }
+    } else {
+      const int soff = t * BC * kstride;  // rows past Nk arrive as zeros (buffer range)
+#pragma unroll
+      for (int it = 0; it < NLOAD; ++it) {
+        char* slot = dst + (wave * NLOAD + it) * 1024;
+        buf_load16_lds(krs, slot, goff[it], soff);
+        buf_load16_lds(vrs, slot + TILE, goff[it], soff);
+      }
+    }
+  };
+
+  // Pipeline state: tile of the current step, the next one (its copy is
+  // issued at the start of the current step) and, paged, the next one's page.
+  int t_cur = n_iter > 0 ? tile_at(0) : -2;
+  int t_nxt = n_iter > 1 ? tile_at(1) : -1;
+  int ph_nxt = page_of(t_nxt);
+
+  auto step = [&](int j, const char* Ks, char* next, const int* Kbad, int* nbad) {
+    const int t = t_cur;
+    if (t_nxt >= 0) load_tile(t_nxt, next, nbad, ph_nxt);
+    const int t_nn = j + 2 < n_iter ? tile_at(j + 2) : -1;
+    ph_nxt = page_of(t_nn);
+    t_cur = t_nxt;
+    t_nxt = t_nn;
     const int k0 = t * BC;
-    if (t + 1 <= t_hi) load_tile(t + 1, next);
     // Tiles wholly outside this wave's band contribute nothing.
-    const bool wave_live = !BAND || (k0 <= wave_row_lo + 31 + off + win_right &&
-                                     k0 + BC - 1 >= wave_row_lo + off - win_left);
+    const bool wave_live = t >= 0 && (!BAND || (k0 <= wave_row_lo + 31 + off + win_right &&
+                                               k0 + BC - 1 >= wave_row_lo + off - win_left));
     if (wave_live) {
       const char* Vs = Ks + TILE;
       // S^T for keys 32 kb .. 32 kb + 31 (s[kb]); with two blocks the
@@ -253,10 +395,17 @@ void fwd_bf16_kernel(
         for (int kb = 0; kb < KB; ++kb) a[kb] = n[kb];
       }
 
-      // Mask the band's edges and the ragged key tail.
+      // Mask the band's edges, the ragged key tail and (paged) the rows of
+      // pages outside the cache.
+      int badm = 0;
+      if constexpr (MODE == kFwdPaged) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) badm |= (Kbad[w] != 0 ? 1 : 0) << w;
+      }
       const bool need_mask =
-          (k0 + BC > Nk) || (BAND && (k0 + BC - 1 > wave_row_lo + off + win_right ||
-                                      k0 < wave_row_lo + 31 + off - win_left));
+          (k0 + BC > Nk) || badm != 0 ||
+          (BAND && (k0 + BC - 1 > wave_row_lo + off + win_right ||
+                    k0 < wave_row_lo + 31 + off - win_left));
       if (need_mask) {
         const int lim = BAND ? min(Nk - 1, qrow + off + win_right) : Nk - 1;
         const int lim_lo = BAND ? qrow + off - win_left : 0;
@@ -264,8 +413,9 @@ void fwd_bf16_kernel(
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key > lim || key < lim_lo) s[kb][r] = -INFINITY;
+            const int kr = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int key = k0 + kr;
+            if (key > lim || key < lim_lo || ((badm >> (kr / WROWS)) & 1)) s[kb][r] = -INFINITY;
           }
       }
 
@@ -331,13 +481,13 @@ void fwd_bf16_kernel(
     __syncthreads();
   };
 
-  if (t_lo <= t_hi) load_tile(t_lo, smem0);
+  if (t_cur >= 0) load_tile(t_cur, smem0, bad0, page_of(t_cur));
   wait_vmem();
   __syncthreads();
   // Unrolled by two so each step's LDS buffers are fixed objects.
-  for (int t = t_lo; t <= t_hi; t += 2) {
-    step(t, smem0, smem1);
-    if (t + 1 <= t_hi) step(t + 1, smem1, smem0);
+  for (int j = 0; j < n_iter; j += 2) {
+    step(j, smem0, smem1, bad0, bad1);
+    if (j + 1 < n_iter) step(j + 1, smem1, smem0, bad1, bad0);
   }
 
   const float l_tot = halves_sum(l_run);
@@ -367,7 +517,7 @@ void fwd_bf16_kernel(
   // Epilogue: one division per row, O in bf16, LSE in natural log.
   if (qrow < Nq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* dst = Op + (size_t)qrow * D;
+    __bf16* dst = Op + (size_t)qrow * (PACKED ? (size_t)H * D : (size_t)D);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -598,13 +748,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(
 template <int D, bool BAND>
 hipError_t launch_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
   constexpr int BC = fwd_bc<D>();
-  const int br = p.block_rows;
-  const int n_qtiles = (a.Nq + br - 1) / br;
   const float sl2 = a.scale * kLog2e;
   const __bf16* q = (const __bf16*)a.Q;
   const __bf16* k = (const __bf16*)a.K;
   const __bf16* v = (const __bf16*)a.V;
   __bf16* o = (__bf16*)a.O;
+  if (a.mode != kFwdDense) {
+    // Packed ragged rows, paged K/V or a sparse block list: four waves,
+    // 128-row query tiles; a.Nq bounds every sequence's query rows.
+    const int n_qt = (a.Nq + 127) / 128;
+    dim3 grid((unsigned)((long long)n_qt * a.B * a.H));
+#define ETA_LAUNCH_MODE(M)                                                                      \
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 4, BC, false, M>), grid, dim3(256), 0, stream, q, \
+                     k, v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qt, a.win_left,         \
+                     a.win_right, 0, 0, nullptr, a.seq)
+    if (a.mode == kFwdRagged) ETA_LAUNCH_MODE(kFwdRagged);
+    else if (a.mode == kFwdPaged) ETA_LAUNCH_MODE(kFwdPaged);
+    else ETA_LAUNCH_MODE(kFwdSparse);
+#undef ETA_LAUNCH_MODE
+    return hipGetLastError();
+  }
   if (a.n_chunks > 0) {
     // Key split: always four waves, 128-row query tiles (whatever the
     // unsplit plan's workgroup size), the tiling the host sized the
@@ -612,9 +775,9 @@ hipError_t launch_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
     const int n_qt = (a.Nq + 127) / 128;
     float* part = (float*)a.workspace;
     dim3 grid((unsigned)((long long)a.split_units * a.B * a.H));
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 4, BC, true>), grid, dim3(256), 0, stream, q, k, v,
-                       o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qt, a.win_left,
-                       a.win_right, a.chunk_tiles, a.n_chunks, part);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 4, BC, true, kFwdDense>), grid, dim3(256), 0, stream,
+                       q, k, v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qt, a.win_left,
+                       a.win_right, a.chunk_tiles, a.n_chunks, part, FwdSeqArgs{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int rpb = 256 / (D / 4);
@@ -624,15 +787,18 @@ hipError_t launch_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
                        n_qt, a.n_chunks, a.chunk_tiles, a.band, a.win_left, a.win_right);
     return hipGetLastError();
   }
+  const int br = p.block_rows;  // the planner's tile: 64 or 128 query rows
+  if (br != 64 && br != 128) return hipErrorInvalidValue;
+  const int n_qtiles = (a.Nq + br - 1) / br;
   dim3 grid((unsigned)(n_qtiles * a.B * a.H));
   if (p.waves == 4) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 4, BC, false>), grid, dim3(256), 0, stream, q, k,
-                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, a.win_left,
-                       a.win_right, 0, 0, nullptr);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 4, BC, false, kFwdDense>), grid, dim3(256), 0, stream,
+                       q, k, v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, a.win_left,
+                       a.win_right, 0, 0, nullptr, FwdSeqArgs{});
   } else {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 2, BC, false>), grid, dim3(128), 0, stream, q, k,
-                       v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, a.win_left,
-                       a.win_right, 0, 0, nullptr);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BAND, 2, BC, false, kFwdDense>), grid, dim3(128), 0, stream,
+                       q, k, v, o, a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, a.win_left,
+                       a.win_right, 0, 0, nullptr, FwdSeqArgs{});
   }
   return hipGetLastError();
 }

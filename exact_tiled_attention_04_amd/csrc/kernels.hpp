@@ -10,6 +10,24 @@ namespace eta {
 // A window side with no limit (larger than any sequence the library accepts).
 constexpr int kUnbounded = 1 << 30;
 
+// Extra inputs of the forward's packed-ragged, paged and sparse modes
+// (all zero for dense rows).  Device pointers; sizes are host values.
+struct FwdSeqArgs {
+  const int* cu_q;         // ragged / paged: [num_seqs + 1] query row offsets
+  const int* k_lens;       // ragged: cu_k [num_seqs + 1]; paged: seqlens_k [num_seqs]
+  const int* block_table;  // paged: [num_seqs, max_blocks]
+  const int* row_ptr;      // sparse: [num_layouts, ceil(Nq/128) + 1]
+  const int* col_idx;      // sparse: listed 128-key blocks
+  int total_q, total_k;    // packed row counts
+  int max_blocks, num_blocks, block_size;  // paged cache geometry
+  int num_layouts;         // sparse: layout of (b, h) = (b * H + h) % num_layouts
+  int nnz;                 // sparse: entries of col_idx
+  long long block_stride, token_stride, head_stride;  // paged cache strides (elements)
+};
+
+// Row layout / tile visitation of the bf16 forward (see fwd.hip).
+enum FwdModeTag : int { kFwdDense = 0, kFwdRagged = 1, kFwdPaged = 2, kFwdSparse = 3 };
+
 struct FwdArgs {
   const void* Q;
   const void* K;
@@ -32,6 +50,10 @@ struct FwdArgs {
   int chunk_tiles, n_chunks;
   int split_units;     // (query tile, part) pairs with work (the grid / (B*H))
   void* workspace;
+  // Mode (FwdModeTag) and its extra inputs.  Ragged / paged: B = num_seqs,
+  // Nq = the longest sequence's query rows, Nk unused.
+  int mode;
+  FwdSeqArgs seq;
 };
 
 // Key tiles of width BC seen by the query rows q0 .. q0 + rows - 1: t_lo .. t_hi

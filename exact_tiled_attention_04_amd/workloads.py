@@ -141,6 +141,102 @@ def decode(num_seqs, Hq, Hkv, d, ctx_lo, ctx_hi, block_size=16,
     }
 
 
+def _offsets(lengths):
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    if len(lengths):
+        cu[1:] = torch.cumsum(torch.as_tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    return cu
+
+
+def ragged(q_lens, k_lens, H, Hkv, d, dtype="bf16", seed=0, device="cpu"):
+    """Packed ragged batch: Q [sum q_lens, H, d], then K and V
+    [sum k_lens, Hkv, d] (drawn in that order), with the int32 row offsets
+    cu_q, cu_k [num_seqs + 1] (CPU)."""
+    dt = torch_dtype(dtype)
+    gen = _generator(seed, device)
+    tq, tk = int(sum(q_lens)), int(sum(k_lens))
+    q = _randn((tq, H, d), dt, gen, device)
+    k = _randn((tk, Hkv, d), dt, gen, device)
+    v = _randn((tk, Hkv, d), dt, gen, device)
+    return {"q": q, "k": k, "v": v, "cu_q": _offsets(q_lens), "cu_k": _offsets(k_lens),
+            "max_q": max(int(x) for x in q_lens) if len(q_lens) else 0}
+
+
+def ragged_lengths(num_seqs, lo, hi, seed=0):
+    """num_seqs lengths uniform in [lo, hi] from a seeded CPU generator."""
+    gen = _generator(seed, "cpu")
+    return torch.randint(lo, hi + 1, (num_seqs,), generator=gen).tolist()
+
+
+def paged_prefill(q_lens, k_lens, Hq, Hkv, d, block_size=16, dtype="bf16", seed=0,
+                  device="cpu", poison=False, extra_blocks=0):
+    """Chunked-prefill workload: sequence s has k_lens[s] cached tokens (its
+    q_lens[s] new ones last) in a paged cache laid out as for :func:`decode`.
+
+    Draw order: the permutation of physical blocks (CPU generator), then Q
+    [sum q_lens, Hq, d], K cache, V cache.  With ``poison`` the slots past
+    each context and every block no sequence uses hold NaN.
+    Returns q, k_cache, v_cache (on ``device``), block_table, cu_q, seqlens_k
+    (int32, CPU) and the sizes used.
+    """
+    cpu_gen = _generator(seed, "cpu")
+    pages = [(max(int(c), 0) + block_size - 1) // block_size for c in k_lens]
+    total_pages = sum(pages) + int(extra_blocks)
+    nblk = max(total_pages, 1)
+    perm = torch.randperm(nblk, generator=cpu_gen)
+    table = torch.full((len(k_lens), max(max(pages) if pages else 1, 1)), -1, dtype=torch.int32)
+    off = 0
+    for s, n in enumerate(pages):
+        table[s, :n] = perm[off:off + n].to(torch.int32)
+        off += n
+    dt = torch_dtype(dtype)
+    gen = _generator(seed, device)
+    q = _randn((int(sum(q_lens)), Hq, d), dt, gen, device)
+    k_cache = _randn((nblk, block_size, Hkv, d), dt, gen, device)
+    v_cache = _randn((nblk, block_size, Hkv, d), dt, gen, device)
+    if poison:
+        used = torch.zeros(nblk, dtype=torch.bool)
+        for s, c in enumerate(k_lens):
+            n = pages[s]
+            used[table[s, :n].long()] = True
+            if c > 0 and c % block_size:
+                last = int(table[s, (c - 1) // block_size])
+                k_cache[last, c % block_size:] = float("nan")
+                v_cache[last, c % block_size:] = float("nan")
+        idle = (~used).nonzero().flatten().to(k_cache.device)
+        k_cache[idle] = float("nan")
+        v_cache[idle] = float("nan")
+    return {"q": q, "k_cache": k_cache, "v_cache": v_cache, "block_table": table,
+            "cu_q": _offsets(q_lens), "seqlens_k": torch.as_tensor(k_lens, dtype=torch.int32),
+            "max_q": max(int(x) for x in q_lens), "num_blocks": nblk, "block_size": block_size}
+
+
+def block_sparse_index(n_layouts, n_qblocks, n_kblocks, local, n_global, density, seed=0):
+    """CSR block index of a synthetic local + global + random pattern ([AK]
+    sparse-attention paragraph: sliding windows, global plus local patterns).
+
+    Query block r (bottom-right aligned onto key block c_r = r + n_kblocks -
+    n_qblocks) lists key blocks c_r - local + 1 .. c_r, the first ``n_global``
+    blocks, and every other block with probability ``density`` (seeded CPU
+    draws, one per candidate).  Returns row_ptr int32 [n_layouts,
+    n_qblocks + 1] (offsets into the shared col_idx) and col_idx int32.
+    """
+    gen = _generator(seed, "cpu")
+    row_ptr = torch.zeros((n_layouts, n_qblocks + 1), dtype=torch.int32)
+    cols = []
+    for lay in range(n_layouts):
+        draws = torch.rand((n_qblocks, n_kblocks), generator=gen)
+        for r in range(n_qblocks):
+            row_ptr[lay, r] = len(cols)
+            diag = r + n_kblocks - n_qblocks
+            for c in range(n_kblocks):
+                near = diag - local < c <= diag
+                if near or c < n_global or draws[r, c] < density:
+                    cols.append(c)
+        row_ptr[lay, n_qblocks] = len(cols)
+    return row_ptr, torch.as_tensor(cols, dtype=torch.int32)
+
+
 # The five workloads the pages' shapes call for (name -> keyword arguments).
 WORKLOADS = {
     "single_head_f32_n512_d64": dict(

@@ -139,6 +139,86 @@ attn_status_t attn_fwd_splitkv(const void* Q, const void* K, const void* V, void
                                void* stream);
 
 /*
+ * Forward over a ragged (variable-length) batch in packed layout.  "Modern
+ * attention kernels", "Numerical validation" (ragged sequence boundaries)
+ * and "Paged attention changes addressing" (a serving engine runs tiled
+ * prefill over many sequences at once).  Each sequence is its own attention
+ * problem, with the causal/band alignment of attn_fwd_local inside it.
+ *   Q, O         [total_q, H, d] bf16 (device): sequence s owns rows
+ *                cu_seqlens_q[s] .. cu_seqlens_q[s+1] - 1.
+ *   K, V         [total_k, Hkv, d] bf16 (device): sequence s owns rows
+ *                cu_seqlens_k[s] .. cu_seqlens_k[s+1] - 1.
+ *   LSE          [H, total_q] float32 output (device).
+ *   cu_seqlens_q, cu_seqlens_k: int32 [num_seqs + 1] on the device,
+ *                non-decreasing, starting at 0 and ending at total_q
+ *                (total_k).  Offsets are clamped into the tensors, so bad
+ *                offsets give wrong rows, never out-of-range accesses.
+ *   max_seqlen_q bound on every sequence's query count (sizes the grid);
+ *                rows past it are not computed.  1 <= max_seqlen_q <= total_q.
+ *   window_left, window_right: as attn_fwd_local ((-1, 0) = causal,
+ *                (-1, -1) = no mask).  A sequence with no keys gets O = 0,
+ *                LSE = -inf on its rows.
+ *   dtype must be BF16; d in {64, 128}; H % Hkv == 0; total_q*H*d*2 and
+ *   total_k*Hkv*d*2 below 2 GiB (else ATTN_ERR_UNSUPPORTED).
+ */
+attn_status_t attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int num_seqs, int total_q, int total_k, int max_seqlen_q, int H,
+                              int Hkv, int d, float scale, int window_left, int window_right,
+                              attn_dtype_t dtype, void* stream);
+
+/*
+ * Prefill of a ragged batch against a paged KV cache (chunked prefill): the
+ * combination "Modern attention kernels", "Paged attention changes
+ * addressing" names for a serving engine.  Sequence s holds seqlens_k[s]
+ * tokens in the cache (the new ones included, already written); its
+ * cu_seqlens_q[s+1] - cu_seqlens_q[s] query rows are the LAST positions of
+ * that context (bottom-right alignment).  One query row per sequence is
+ * paged decode; as many rows as tokens is a full prefill.
+ *   Q, O         [total_q, Hq, d] bf16; LSE [Hq, total_q] float32.
+ *   K_cache, V_cache, block_table, num_blocks, max_blocks_per_seq and the
+ *                strides: as attn_decode_paged; additionally block_size must
+ *                be a multiple of 16 (else ATTN_ERR_UNSUPPORTED) and
+ *                token_stride < 2^24.  As in attn_decode_paged, a live token
+ *                whose block-table entry lies outside [0, num_blocks) is
+ *                skipped (probability 0) and never read.
+ *   seqlens_k    int32 [num_seqs] on the device; clamped to
+ *                [0, max_blocks_per_seq * block_size].
+ *   cu_seqlens_q, max_seqlen_q, window sides, errors: as attn_fwd_varlen.
+ */
+attn_status_t attn_prefill_paged(const void* Q, const void* K_cache, const void* V_cache,
+                                 const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                 const int32_t* seqlens_k, void* O, float* LSE, int num_seqs,
+                                 int total_q, int max_seqlen_q, int Hq, int Hkv, int d,
+                                 int block_size, int num_blocks, int max_blocks_per_seq,
+                                 int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                                 float scale, int window_left, int window_right,
+                                 attn_dtype_t dtype, void* stream);
+
+/*
+ * Forward restricted to listed score blocks of 128 queries x 128 keys.
+ * "Modern attention kernels", "Kernel structure": arbitrary sparse masks need
+ * an index structure telling the kernel which blocks exist; "Paged attention
+ * changes addressing": sparse attention visits selected score blocks.
+ *   row_ptr      int32 [num_layouts, ceil(Nq/128) + 1] (device): layout l
+ *                lists for query block r the key blocks
+ *                col_idx[row_ptr[l][r] .. row_ptr[l][r+1] - 1].
+ *   col_idx      int32 [nnz] (device): key-block indices; each block at most
+ *                once per row (order free).  Entries outside
+ *                [0, ceil(Nk/128)) are ignored; offsets are clamped to nnz.
+ *   num_layouts  >= 1; (batch b, head h) uses layout (b*H + h) % num_layouts
+ *                (1: one pattern for all, H: per head, B*H: per batch and head).
+ *   causal != 0 intersects the listed blocks with the bottom-right causal
+ *   mask.  A row with no visible key gets O = 0, LSE = -inf.  Other
+ *   arguments as attn_fwd; dtype must be BF16.
+ */
+attn_status_t attn_fwd_block_sparse(const void* Q, const void* K, const void* V, void* O,
+                                    float* LSE, int B, int H, int Hkv, int Nq, int Nk, int d,
+                                    float scale, int causal, const int32_t* row_ptr,
+                                    const int32_t* col_idx, int num_layouts, int nnz,
+                                    attn_dtype_t dtype, void* stream);
+
+/*
  * Bytes of workspace attn_decode_paged needs for these sizes (0 when the
  * arguments are invalid).  chunk_tokens as for attn_decode_paged.
  */

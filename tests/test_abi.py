@@ -208,3 +208,77 @@ def test_fwd_splitkv_validation(lib, cpu_only, kw, status):
                               kw.get("left", -1), 0, kw.get("dtype", attn.ATTN_DTYPE_BF16), chunk,
                               kw.get("ws", FAKE), kw.get("ws_bytes", 1 << 30), NULL)
     assert st == status
+
+
+def _varlen(lib, q=FAKE, k=FAKE, cu_q=FAKE, cu_k=FAKE, num_seqs=2, total_q=16, total_k=20,
+            max_q=8, H=2, Hkv=1, d=64, scale=0.125, wl=-1, wr=0, dtype=attn.ATTN_DTYPE_BF16):
+    return lib.attn_fwd_varlen(q, k, FAKE, FAKE, FAKE, cu_q, cu_k, num_seqs, total_q, total_k,
+                               max_q, H, Hkv, d, scale, wl, wr, dtype, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), attn.ATTN_ERR_INVALID_ARG),
+    (dict(cu_k=NULL), attn.ATTN_ERR_INVALID_ARG),
+    (dict(k=MISALIGNED), attn.ATTN_ERR_INVALID_ARG),
+    (dict(num_seqs=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(max_q=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(max_q=17), attn.ATTN_ERR_INVALID_ARG),       # longer than the packed batch
+    (dict(total_k=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(H=3, Hkv=2), attn.ATTN_ERR_INVALID_ARG),
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=attn.ATTN_DTYPE_F32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(wl=-2), attn.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), attn.ATTN_ERR_INVALID_ARG),
+    (dict(total_q=1 << 22, H=64, d=128, max_q=8), attn.ATTN_ERR_UNSUPPORTED),  # > 2 GiB packed
+])
+def test_fwd_varlen_validation(lib, cpu_only, kw, status):
+    assert _varlen(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def _prefill_paged(lib, q=FAKE, kc=FAKE, table=FAKE, num_seqs=2, total_q=16, max_q=8, Hq=4,
+                   Hkv=2, d=128, bs=16, num_blocks=10, max_blocks=4, strides=None, wl=-1, wr=0,
+                   dtype=attn.ATTN_DTYPE_BF16):
+    if strides is None:
+        strides = (bs * Hkv * d, Hkv * d, d)
+    return lib.attn_prefill_paged(q, kc, FAKE, table, FAKE, FAKE, FAKE, FAKE, num_seqs, total_q,
+                                  max_q, Hq, Hkv, d, bs, num_blocks, max_blocks, *strides, 0.088,
+                                  wl, wr, dtype, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(table=NULL), attn.ATTN_ERR_INVALID_ARG),
+    (dict(kc=MISALIGNED), attn.ATTN_ERR_INVALID_ARG),
+    (dict(bs=8), attn.ATTN_ERR_UNSUPPORTED),            # pages must hold a multiple of 16 tokens
+    (dict(bs=24), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(num_blocks=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(strides=(16 * 2 * 128, 128, 128)), attn.ATTN_ERR_INVALID_ARG),  # token stride < Hkv*d
+    (dict(strides=(100, 256, 128)), attn.ATTN_ERR_INVALID_ARG),           # overlapping blocks
+    (dict(Hq=3, Hkv=2), attn.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=attn.ATTN_DTYPE_F32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=80), attn.ATTN_ERR_UNSUPPORTED),
+])
+def test_prefill_paged_validation(lib, cpu_only, kw, status):
+    assert _prefill_paged(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def _sparse(lib, rp=FAKE, ci=FAKE, B=1, H=2, Hkv=1, Nq=256, Nk=256, d=64, layouts=1, nnz=3,
+            dtype=attn.ATTN_DTYPE_BF16):
+    return lib.attn_fwd_block_sparse(FAKE, FAKE, FAKE, FAKE, FAKE, B, H, Hkv, Nq, Nk, d, 0.125, 1,
+                                     rp, ci, layouts, nnz, dtype, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rp=NULL), attn.ATTN_ERR_INVALID_ARG),
+    (dict(ci=NULL), attn.ATTN_ERR_INVALID_ARG),
+    (dict(rp=ctypes.c_void_p((1 << 20) + 2)), attn.ATTN_ERR_INVALID_ARG),
+    (dict(layouts=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(nnz=-1), attn.ATTN_ERR_INVALID_ARG),
+    (dict(Nq=0), attn.ATTN_ERR_INVALID_ARG),
+    (dict(d=32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=attn.ATTN_DTYPE_F32), attn.ATTN_ERR_UNSUPPORTED),
+])
+def test_block_sparse_validation(lib, cpu_only, kw, status):
+    assert _sparse(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
