@@ -9,10 +9,22 @@ resident in HBM:
   2. paged GQA decode, 64 sequences, Hq=32, Hkv=8, d=128, contexts uniform
      in [4096, 32768], 16-token pages via a seeded permutation (KV GB/s and
      fraction of HBM peak);
-  3. causal bf16 backward, B=2, H=16, N=4096, d=128 (TFLOP/s).
+  3. causal bf16 backward, B=2, H=16, N=4096, d=128 (TFLOP/s);
 Each call is bracketed by HIP events recorded on the stream the library
 launches on (torch's current stream); the K timed steps are bracketed by a
 device synchronisation on both sides.  Rank 0 prints one JSON line.
+
+After the timed steps, the entry points beyond the hot path are timed the
+same way in a loop of their own (K calls each, after W warm-up calls), so
+they do not change the conditions the step is measured under:
+  * the 4-head variant of (1) through the key split;
+  * a packed ragged causal prefill (16 sequences of 512..8192 tokens, GQA
+    32/8, d=128);
+  * a chunked prefill through the paged cache (16 sequences, 512..2048 new
+    tokens after 2048..8192 cached ones, 16-token pages);
+  * a block-sparse causal forward (B=1, H=32, N=8192, d=128, per-head local
+    + global + random 128x128 blocks).
+Their FLOPs count the (query, key) pairs the masks leave visible, times 4 d.
 
 FLOPs follow "Attention kernels" (the FLOPs paragraph): 4 N^2 d per head,
 halved under the causal mask; the backward also reports its algorithmic
@@ -140,6 +152,40 @@ def main():
                       dtype=torch.uint8, device=dev)
     bwd_flops_fwd_equiv = 4.0 * bw["B"] * bw["H"] * bw["Nq"] * bw["Nk"] * bw["d"] / 2.0
     bwd_flops_algo = 2.5 * bwd_flops_fwd_equiv
+
+    # Packed ragged prefill, chunked prefill through the paged cache, and
+    # block-sparse visitation.
+    vw = workloads.WORKLOADS["varlen_causal_bf16_s16_h32_hkv8_d128"]
+    vlens = workloads.ragged_lengths(vw["num_seqs"], vw["len_lo"], vw["len_hi"], seed=vw["seed"] + 1)
+    rg = workloads.ragged(vlens, vlens, vw["H"], vw["Hkv"], vw["d"], seed=vw["seed"], device=str(dev))
+    rg_cu = rg["cu_q"].to(dev)
+    rg_o = torch.empty_like(rg["q"])
+    rg_lse = torch.empty((vw["H"], rg["q"].shape[0]), dtype=torch.float32, device=dev)
+    varlen_flops = 4.0 * vw["d"] * vw["H"] * sum(n * (n + 1) / 2 for n in vlens)
+
+    pw = workloads.WORKLOADS["paged_prefill_causal_bf16_s16_hq32_hkv8_d128"]
+    pp = workloads.serving_prefill(pw["num_seqs"], pw["q_lo"], pw["q_hi"], pw["ctx_lo"],
+                                   pw["ctx_hi"], pw["Hq"], pw["Hkv"], pw["d"],
+                                   block_size=pw["block_size"], seed=pw["seed"], device=str(dev))
+    pp_bt, pp_cu, pp_k = (pp["block_table"].to(dev), pp["cu_q"].to(dev), pp["seqlens_k"].to(dev))
+    pp_o = torch.empty_like(pp["q"])
+    pp_lse = torch.empty((pw["Hq"], pp["q"].shape[0]), dtype=torch.float32, device=dev)
+    # Query row i of a chunk of q rows sits at position i + k - q and sees keys 0 .. that position.
+    paged_flops = 4.0 * pw["d"] * pw["Hq"] * sum(
+        q_ * (k_ - q_) + q_ * (q_ + 1) / 2 for q_, k_ in zip(pp["q_lens"], pp["k_lens"]))
+
+    xw = workloads.WORKLOADS["block_sparse_causal_bf16_b1_h32_n8192_d128"]
+    xq, xk, xv = workloads.prefill(xw["B"], xw["H"], xw["Hkv"], xw["N"], xw["N"], xw["d"],
+                                   seed=xw["seed"], device=str(dev))
+    nb = xw["N"] // 128
+    x_rp, x_ci = workloads.block_sparse_index(xw["layouts"], nb, nb, xw["local"], xw["n_global"],
+                                              xw["density"], seed=xw["seed"])
+    sparse_flops = 4.0 * xw["d"] * xw["B"] * sum(
+        _sparse_pairs(x_rp[h % xw["layouts"]].tolist(), x_ci.tolist()) for h in range(xw["H"]))
+    sparse_density = sparse_flops / (4.0 * xw["d"] * xw["B"] * xw["H"] * xw["N"] * (xw["N"] + 1) / 2)
+    x_rp, x_ci = x_rp.to(dev), x_ci.to(dev)
+    xo = torch.empty_like(xq)
+    xlse = torch.empty((xw["B"], xw["H"], xw["N"]), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     def step(events=None):
@@ -153,13 +199,23 @@ def main():
         attn.attn_bwd(bq, bk, bv, bo, bdo, blse, bw["scale"], True, dq=bdq, dk=bdk, dv=bdv,
                       workspace=bws, stream=stream)
         if e: e[3].record(stream)
-        attn.attn_fwd_splitkv(sq, sk, sv, sw["scale"], -1, 0, out=so, lse=slse, workspace=sws,
-                              stream=stream)
-        if e: e[4].record(stream)
+
+    extras = [
+        ("fwd_small_grid", split_flops, lambda: attn.attn_fwd_splitkv(
+            sq, sk, sv, sw["scale"], -1, 0, out=so, lse=slse, workspace=sws, stream=stream)),
+        ("varlen", varlen_flops, lambda: attn.attn_fwd_varlen(
+            rg["q"], rg["k"], rg["v"], rg_cu, rg_cu, rg["max_q"], vw["scale"], -1, 0, out=rg_o,
+            lse=rg_lse, stream=stream)),
+        ("paged_prefill", paged_flops, lambda: attn.attn_prefill_paged(
+            pp["q"], pp["k_cache"], pp["v_cache"], pp_bt, pp_cu, pp_k, pp["max_q"], pw["scale"],
+            -1, 0, out=pp_o, lse=pp_lse, stream=stream)),
+        ("block_sparse", sparse_flops, lambda: attn.attn_fwd_block_sparse(
+            xq, xk, xv, xw["scale"], True, x_rp, x_ci, out=xo, lse=xlse, stream=stream)),
+    ]
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -171,11 +227,24 @@ def main():
         s = sorted(vals)
         return s[len(s) // 2]
 
+    extra = {}
+    for name, flops, call in extras:
+        for _ in range(args.warmup):
+            call()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(args.steps):
+            call()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+        extra[name] = (sum(ms) / len(ms), med(ms), flops)
+
     fwd_ms = [ev[0].elapsed_time(ev[1]) for ev in events]
     dec_ms = [ev[1].elapsed_time(ev[2]) for ev in events]
     bwd_ms = [ev[2].elapsed_time(ev[3]) for ev in events]
-    split_ms = [ev[3].elapsed_time(ev[4]) for ev in events]
-    split_avg = sum(split_ms) / len(split_ms)
+    split_avg = extra["fwd_small_grid"][0]
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     dec_avg = sum(dec_ms) / len(dec_ms)
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
@@ -205,8 +274,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "causal_bf16_b1_h32_n8192_d128 (headline) + "
-                        "paged_gqa_decode_bf16_s64_hq32_hkv8_d128 + causal_bwd_bf16_b2_h16_n4096_d128"
-                        " + causal_bf16_b1_h4_n8192_d128 (key split)",
+                        "paged_gqa_decode_bf16_s64_hq32_hkv8_d128 + causal_bwd_bf16_b2_h16_n4096_d128",
             "B": fw["B"], "H": fw["H"], "N": fw["Nq"], "d": fw["d"], "causal": True,
             "plan": attn.attn_plan_describe(attn.ATTN_PHASE_FWD, fw["B"], fw["H"], fw["Hkv"],
                                             fw["Nq"], fw["Nk"], fw["d"], True),
@@ -252,13 +320,40 @@ def main():
             "workspace_bytes": sws_bytes,
         },
         "per_call_ms_median": {"fwd": round(med(fwd_ms), 4), "decode": round(med(dec_ms), 4),
-                               "bwd": round(med(bwd_ms), 4), "fwd_small_grid": round(med(split_ms), 4)},
+                               "bwd": round(med(bwd_ms), 4),
+                               **{k: round(v[1], 4) for k, v in extra.items()}},
     }
+    for name, workload, note in [
+            ("varlen", "varlen_causal_bf16_s16_h32_hkv8_d128 (attn_fwd_varlen)",
+             f"{len(vlens)} packed sequences, {sum(vlens)} tokens"),
+            ("paged_prefill", "paged_prefill_causal_bf16_s16_hq32_hkv8_d128 (attn_prefill_paged)",
+             f"{sum(pp['q_lens'])} new tokens over {sum(pp['k_lens'])} cached"),
+            ("block_sparse", "block_sparse_causal_bf16_b1_h32_n8192_d128 (attn_fwd_block_sparse)",
+             f"visible pairs {100 * sparse_density:.1f}% of causal")]:
+        avg, _, flops = extra[name]
+        tf = flops / (avg * 1e-3) / 1e12
+        result[name] = {"workload": workload, "value": round(tf, 2), "unit": "TFLOP/s",
+                        "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "avg_call_ms": round(avg, 4), "flop_per_call": flops, "note": note}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, fw, args.cpu_heads)
     print(json.dumps(result))
     return 0
+
+
+def _sparse_pairs(row_ptr, col_idx, block=128):
+    """Causal (query, key) pairs inside the listed blocks of one layout with
+    Nq = Nk (square blocks): blocks below the diagonal are full, diagonal
+    blocks hold a triangle, blocks above hold none."""
+    pairs = 0
+    for r in range(len(row_ptr) - 1):
+        for c in col_idx[row_ptr[r]:row_ptr[r + 1]]:
+            if c < r:
+                pairs += block * block
+            elif c == r:
+                pairs += block * (block + 1) // 2
+    return pairs
 
 
 def cpu_baseline(q, k, v, fw, heads):

@@ -211,6 +211,21 @@ def paged_prefill(q_lens, k_lens, Hq, Hkv, d, block_size=16, dtype="bf16", seed=
             "max_q": max(int(x) for x in q_lens), "num_blocks": nblk, "block_size": block_size}
 
 
+def serving_prefill(num_seqs, q_lo, q_hi, ctx_lo, ctx_hi, Hq, Hkv, d, block_size=16,
+                    dtype="bf16", seed=0, device="cpu"):
+    """Chunked prefill of a serving batch: new-token counts uniform in
+    [q_lo, q_hi] (seed + 1), prior cached context uniform in [ctx_lo, ctx_hi]
+    (seed + 2); each sequence's context is prior + new tokens, then
+    :func:`paged_prefill` with ``seed``."""
+    q_lens = ragged_lengths(num_seqs, q_lo, q_hi, seed=seed + 1)
+    prior = ragged_lengths(num_seqs, ctx_lo, ctx_hi, seed=seed + 2)
+    k_lens = [q + p for q, p in zip(q_lens, prior)]
+    w = paged_prefill(q_lens, k_lens, Hq, Hkv, d, block_size=block_size, dtype=dtype, seed=seed,
+                      device=device)
+    w["q_lens"], w["k_lens"] = q_lens, k_lens
+    return w
+
+
 def block_sparse_index(n_layouts, n_qblocks, n_kblocks, local, n_global, density, seed=0):
     """CSR block index of a synthetic local + global + random pattern ([AK]
     sparse-attention paragraph: sliding windows, global plus local patterns).
@@ -258,6 +273,20 @@ WORKLOADS = {
         kind="decode", num_seqs=64, Hq=32, Hkv=8, d=128, ctx_lo=4096,
         ctx_hi=32768, block_size=16, max_blocks_per_seq=2048, dtype="bf16",
         scale=1.0 / math.sqrt(128.0), seed=0),
+    # Rows beyond the five configurations: the serving-engine combination and
+    # sparse visitation ("Modern attention kernels", "Paged attention changes
+    # addressing"), shaped like the decode and long-prefill workloads.
+    "varlen_causal_bf16_s16_h32_hkv8_d128": dict(
+        kind="varlen", num_seqs=16, len_lo=512, len_hi=8192, H=32, Hkv=8, d=128,
+        dtype="bf16", causal=True, scale=1.0 / math.sqrt(128.0), seed=0),
+    "paged_prefill_causal_bf16_s16_hq32_hkv8_d128": dict(
+        kind="paged_prefill", num_seqs=16, q_lo=512, q_hi=2048, ctx_lo=2048, ctx_hi=8192,
+        Hq=32, Hkv=8, d=128, block_size=16, dtype="bf16", causal=True,
+        scale=1.0 / math.sqrt(128.0), seed=0),
+    "block_sparse_causal_bf16_b1_h32_n8192_d128": dict(
+        kind="block_sparse", B=1, H=32, Hkv=32, N=8192, d=128, layouts=32, local=4,
+        n_global=1, density=0.1, dtype="bf16", causal=True, scale=1.0 / math.sqrt(128.0),
+        seed=0),
     "causal_bwd_bf16_b2_h16_n4096_d128": dict(
         kind="bwd", B=2, H=16, Hkv=16, Nq=4096, Nk=4096, d=128, dtype="bf16",
         causal=True, scale=1.0 / math.sqrt(128.0), seed=0),

@@ -171,15 +171,17 @@ def test_prefill_paged_chunks_compose_full_prefill(gpu):
     check_lse(to64(torch.cat([l1, l2], dim=1)), to64(lse_full), "bf16")
 
 
-@pytest.mark.parametrize("num_seqs,q_lo,q_hi,ctx_lo,ctx_hi", [(16, 512, 2048, 2048, 8192)])
-def test_prefill_paged_serving_shape_sampled(gpu, num_seqs, q_lo, q_hi, ctx_lo, ctx_hi):
-    """The benchmark's serving-shaped workload (GQA 32/8, d = 128, 16-token
-    pages): sampled sequences and query rows against the oracle."""
-    q_lens = workloads.ragged_lengths(num_seqs, q_lo, q_hi, seed=1)
-    prior = workloads.ragged_lengths(num_seqs, ctx_lo, ctx_hi, seed=2)
-    k_lens = [q + p for q, p in zip(q_lens, prior)]
-    w = workloads.paged_prefill(q_lens, k_lens, 32, 8, 128, seed=0, device=str(gpu))
-    scale = 1.0 / math.sqrt(128)
+def test_prefill_paged_serving_shape_sampled(gpu):
+    """The benchmark's serving-shaped workload (16 sequences, GQA 32/8,
+    d = 128, 16-token pages) in the benchmark's launch configuration:
+    sampled sequences and query rows against the oracle."""
+    pw = workloads.WORKLOADS["paged_prefill_causal_bf16_s16_hq32_hkv8_d128"]
+    num_seqs = pw["num_seqs"]
+    w = workloads.serving_prefill(num_seqs, pw["q_lo"], pw["q_hi"], pw["ctx_lo"], pw["ctx_hi"],
+                                  pw["Hq"], pw["Hkv"], pw["d"], block_size=pw["block_size"],
+                                  seed=pw["seed"], device=str(gpu))
+    q_lens, k_lens = w["q_lens"], w["k_lens"]
+    scale = pw["scale"]
     o, lse = _paged(w, gpu, scale, (-1, 0))
     cu = w["cu_q"].tolist()
     rng = np.random.default_rng(0)
@@ -191,8 +193,32 @@ def test_prefill_paged_serving_shape_sampled(gpu, num_seqs, q_lo, q_hi, ctx_lo, 
         # Row i of the chunk sits at position i + k - q and sees keys 0 .. that position.
         pos = rows + k_lens[s] - q_lens[s]
         vis = (np.arange(k_lens[s])[None, :] <= pos[:, None])[None, None]
-        qs = to64(w["q"][cu[s] + rows]).transpose(1, 0, 2)[None]
+        qs = to64(w["q"][torch.as_tensor(cu[s] + rows)]).transpose(1, 0, 2)[None]
         o_ref, lse_ref = oracle.forward(qs, kk.transpose(1, 0, 2)[None], vv.transpose(1, 0, 2)[None],
                                         scale, False, mask=vis)
-        check_out(to64(o[cu[s] + rows]).transpose(1, 0, 2), o_ref[0], "bf16")
-        check_lse(to64(lse[:, cu[s] + rows]), lse_ref[0], "bf16")
+        check_out(to64(o[torch.as_tensor(cu[s] + rows)]).transpose(1, 0, 2), o_ref[0], "bf16")
+        check_lse(to64(lse[:, torch.as_tensor(cu[s] + rows)]), lse_ref[0], "bf16")
+
+
+def test_varlen_bench_shape_sampled(gpu):
+    """The benchmark's packed ragged workload (16 sequences of 512..8192
+    tokens, GQA 32/8, d = 128, causal) in the benchmark's launch
+    configuration: sampled sequences and rows against the oracle."""
+    vw = workloads.WORKLOADS["varlen_causal_bf16_s16_h32_hkv8_d128"]
+    lens = workloads.ragged_lengths(vw["num_seqs"], vw["len_lo"], vw["len_hi"], seed=vw["seed"] + 1)
+    w = workloads.ragged(lens, lens, vw["H"], vw["Hkv"], vw["d"], seed=vw["seed"], device=str(gpu))
+    o, lse = attn.attn_fwd_varlen(w["q"], w["k"], w["v"], w["cu_q"].to(gpu), w["cu_k"].to(gpu),
+                                  w["max_q"], vw["scale"], -1, 0)
+    torch.cuda.synchronize()
+    cu = w["cu_q"].tolist()
+    rng = np.random.default_rng(2)
+    for s in rng.choice(vw["num_seqs"], 3, replace=False):
+        n = lens[s]
+        rows = np.sort(rng.choice(n, 8, replace=False))
+        kk = to64(w["k"][cu[s]:cu[s + 1]]).transpose(1, 0, 2)[None]
+        vv = to64(w["v"][cu[s]:cu[s + 1]]).transpose(1, 0, 2)[None]
+        vis = (np.arange(n)[None, :] <= rows[:, None])[None, None]
+        qs = to64(w["q"][torch.as_tensor(cu[s] + rows)]).transpose(1, 0, 2)[None]
+        o_ref, lse_ref = oracle.forward(qs, kk, vv, vw["scale"], False, mask=vis)
+        check_out(to64(o[torch.as_tensor(cu[s] + rows)]).transpose(1, 0, 2), o_ref[0], "bf16")
+        check_lse(to64(lse[:, torch.as_tensor(cu[s] + rows)]), lse_ref[0], "bf16")

@@ -97,3 +97,29 @@ def test_block_sparse_long_rows_refill(gpu):
     o_ref, lse_ref = _ref(q, k, v, scale, True, row_ptr, col_idx)
     check_out(to64(o), o_ref, "bf16")
     check_lse(to64(lse), lse_ref, "bf16")
+
+
+def test_block_sparse_bench_shape_sampled(gpu):
+    """The benchmark's block-sparse workload (B=1, H=32, N=8192, d=128,
+    per-head local + global + random blocks, causal) in the benchmark's
+    launch configuration: sampled heads and rows against the oracle, with
+    the block mask and the causal mask written out as one boolean mask."""
+    bw = workloads.WORKLOADS["block_sparse_causal_bf16_b1_h32_n8192_d128"]
+    N, d, H = bw["N"], bw["d"], bw["H"]
+    q, k, v = workloads.prefill(bw["B"], H, bw["Hkv"], N, N, d, seed=bw["seed"], device=str(gpu))
+    row_ptr, col_idx = workloads.block_sparse_index(bw["layouts"], N // 128, N // 128, bw["local"],
+                                                    bw["n_global"], bw["density"], seed=bw["seed"])
+    o, lse = _run(gpu, q, k, v, bw["scale"], True, row_ptr, col_idx)
+    blocks = oracle.block_mask_from_index(row_ptr.numpy(), col_idx.numpy(), N // 128, N // 128)
+    rng = np.random.default_rng(1)
+    for h in rng.choice(H, 3, replace=False):
+        rows = np.sort(rng.choice(N, 12, replace=False))
+        cols = np.arange(N)
+        vis = blocks[h % bw["layouts"]][rows[:, None] // 128, cols[None, :] // 128]
+        vis &= cols[None, :] <= rows[:, None]
+        kk = to64(k[0, h])[None, None]
+        vv = to64(v[0, h])[None, None]
+        o_ref, lse_ref = oracle.forward(to64(q[0, h, torch.as_tensor(rows)])[None, None], kk, vv, bw["scale"], False,
+                                        mask=vis[None, None])
+        check_out(to64(o[0, h, torch.as_tensor(rows)]), o_ref[0, 0], "bf16")
+        check_lse(to64(lse[0, h, torch.as_tensor(rows)]), lse_ref[0, 0], "bf16")
