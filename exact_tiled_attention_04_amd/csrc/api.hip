@@ -369,6 +369,13 @@ attn_status_t attn_prefill_paged(const void* Q, const void* K_cache, const void*
   a.seq.max_blocks = max_blocks_per_seq;
   a.seq.num_blocks = num_blocks;
   a.seq.block_size = block_size;
+  // Division of 31-bit keys by block_size: m = floor(2^(31+l) / bs) + 1 with
+  // l = ceil(log2 bs) gives key / bs = (key * m) >> (31 + l) exactly, since
+  // the error key * (m - 2^(31+l)/bs) / 2^(31+l) stays below 1/bs; m < 2^32.
+  int l = 0;
+  while ((1LL << l) < block_size) ++l;
+  a.seq.page_magic = (unsigned)((1ULL << (31 + l)) / (unsigned long long)block_size + 1);
+  a.seq.page_shift = 31 + l;
   a.seq.block_stride = block_stride;
   a.seq.token_stride = token_stride;
   a.seq.head_stride = head_stride;

@@ -94,6 +94,45 @@ __device__ __forceinline__ void split_unit(int u, int n_qtiles, int BR, int Nq, 
   chunk_out = __builtin_amdgcn_readfirstlane(chunk);
 }
 
+// Page of key position `key` (0 <= key < 2^31): key / block_size by a
+// multiply-high with the host's magic number m = floor(2^(31+l) / bs) + 1,
+// l = ceil(log2 bs), exact for every 31-bit key; scalar instructions only
+// (a plain division is a long VALU sequence).
+__device__ __forceinline__ int page_div(int key, const FwdSeqArgs& sq) {
+  return (int)(((unsigned long long)(unsigned)key * sq.page_magic) >> sq.page_shift);
+}
+
+// Query tile and (batch, head) of workgroup wg, heaviest (last) query tiles
+// first.  Workgroups reach the eight XCDs round robin (wg % 8), and each XCD
+// has its own L2.  When the (batch, KV head) pairs divide evenly over the
+// XCDs, XCD x takes the pairs p = x, x + 8, ... and, for each, all query heads
+// of the group next to each other: the heads that share K and V run on one
+// L2 at the same time, each pair's K/V is fetched by one XCD, and every XCD
+// gets the same share of every sequence.  Within an XCD the order is either
+// query-tile layers across its pairs (dense rows: the heaviest tiles of every
+// head first) or PAIR_MAJOR, all tiles of one pair before the next (packed
+// sequences of different lengths: a pair's tiles stream its K/V together).
+// Otherwise consecutive workgroups take consecutive (batch, head) indices.
+template <bool PAIR_MAJOR>
+__device__ __forceinline__ void grid_tile(int wg, int n_qtiles, int B, int H, int Hkv, int& qt,
+                                          int& bh) {
+  const int P = B * Hkv;
+  if ((P & 7) == 0) {
+    const int G = H / Hkv;
+    const int x = wg & 7, k = wg >> 3;
+    const int hg = k % G, kk = k / G;
+    const int per = P >> 3;
+    const int pp = PAIR_MAJOR ? kk / n_qtiles : kk % per;
+    const int qt_rev = PAIR_MAJOR ? kk % n_qtiles : kk / per;
+    const int p = pp * 8 + x;
+    qt = n_qtiles - 1 - qt_rev;
+    bh = (p / Hkv) * H + (p % Hkv) * G + hg;
+  } else {
+    qt = n_qtiles - 1 - wg / (B * H);
+    bh = wg % (B * H);
+  }
+}
+
 // The running maximum is a reference point, not necessarily the exact row
 // maximum: it moves (and the accumulator is rescaled) only when a tile's
 // maximum exceeds it by more than kSlack in base-2 units.  o / l and
@@ -168,8 +207,7 @@ void fwd_bf16_kernel(
     split_unit<BAND>(wg / BH, n_qtiles, BR, Nq, Nk, BC, win_left, win_right, chunk_tiles, lane,
                      qt, chunk);
   } else {
-    qt = n_qtiles - 1 - wg / BH;
-    bh = wg % BH;
+    grid_tile<MODE == kFwdRagged || MODE == kFwdPaged>(wg, n_qtiles, B, H, Hkv, qt, bh);
   }
   const int b = bh / H;       // batch, or sequence of a packed batch
   const int h = bh % H;
@@ -306,7 +344,7 @@ void fwd_bf16_kernel(
       if (t < 0) return -1;
       const int key = t * BC + wave * WROWS;
       if (key >= Nk) return -1;
-      return sq.block_table[(size_t)b * sq.max_blocks + key / sq.block_size];
+      return sq.block_table[(size_t)b * sq.max_blocks + page_div(key, sq)];
     } else {
       return 0;
     }
@@ -325,7 +363,8 @@ void fwd_bf16_kernel(
       if (bad) live = 0;
       if (lane == 0) bad_dst[wave] = bad ? 1 : 0;
       unsigned long long eo = live ? (unsigned long long)phys * sq.block_stride +
-                                         (unsigned long long)(key % sq.block_size) * sq.token_stride +
+                                         (unsigned long long)(key - page_div(key, sq) * sq.block_size) *
+                                             sq.token_stride +
                                          (unsigned long long)g * sq.head_stride
                                    : 0;
       // All of it is wave-uniform; readfirstlane lets the compiler keep the

@@ -20,6 +20,8 @@ struct FwdSeqArgs {
   const int* col_idx;      // sparse: listed 128-key blocks
   int total_q, total_k;    // packed row counts
   int max_blocks, num_blocks, block_size;  // paged cache geometry
+  unsigned page_magic;     // paged: key / block_size == (key * page_magic) >> page_shift
+  int page_shift;
   int num_layouts;         // sparse: layout of (b, h) = (b * H + h) % num_layouts
   int nnz;                 // sparse: entries of col_idx
   long long block_stride, token_stride, head_stride;  // paged cache strides (elements)
