@@ -251,17 +251,18 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale, wi
 
 def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, max_seqlen_q,
                        scale, window_left=-1, window_right=-1, num_blocks=None, strides=None,
-                       out=None, lse=None, stream=None):
+                       out=None, lse=None, stream=None, cache_dims=None):
     """Ragged queries q [total_q, Hq, d] against a paged cache
     [num_blocks, block_size, Hkv, d] (or ``strides`` = (block, token, head) in
-    elements); block_table int32 [num_seqs, max_blocks]; cu_seqlens_q int32
+    elements, with ``cache_dims`` = (num_blocks, block_size, Hkv) for other
+    shapes); block_table int32 [num_seqs, max_blocks]; cu_seqlens_q int32
     [num_seqs + 1]; seqlens_k int32 [num_seqs].  Each sequence's queries are
     the last positions of its cached context.  Returns O and LSE [Hq, total_q]."""
     lib = load_library()
     _need_device(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k)
     _need_int32(block_table, cu_seqlens_q, seqlens_k)
     total_q, Hq, d = q.shape
-    nb, block_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    nb, block_size, Hkv = _cache_dims(k_cache, cache_dims)
     num_blocks = nb if num_blocks is None else num_blocks
     num_seqs = cu_seqlens_q.numel() - 1
     if seqlens_k.numel() != num_seqs or block_table.shape[0] != num_seqs:
@@ -304,21 +305,29 @@ def attn_decode_paged_workspace_size(num_seqs, Hq, d, max_context, chunk_tokens=
                                                                chunk_tokens))
 
 
+def _cache_dims(k_cache, cache_dims):
+    """(num_blocks, block_size, Hkv): from a [blocks, slots, heads, d] shape, or
+    given explicitly for other layouts (e.g. head-major pages via strides)."""
+    if cache_dims is not None:
+        return tuple(int(x) for x in cache_dims)
+    return k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+
+
 def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, scale, max_context,
                       chunk_tokens=0, strides=None, out=None, lse=None, workspace=None,
-                      stream=None):
+                      stream=None, cache_dims=None):
     """Paged GQA decode.
 
     q [num_seqs, Hq, d]; k_cache, v_cache [num_blocks, block_size, Hkv, d]
     (or any layout described by ``strides`` = (block, token, head) in
-    elements, with ``k_cache`` shaped so that dim 0 counts blocks, dim 1 the
-    slots and dim 2 the KV heads); block_table int32 [num_seqs, max_blocks];
-    context_lens int32 [num_seqs] on the device.
+    elements, with ``cache_dims`` = (num_blocks, block_size, Hkv) when the
+    tensor's shape is not [blocks, slots, heads, d]); block_table int32
+    [num_seqs, max_blocks]; context_lens int32 [num_seqs] on the device.
     """
     lib = load_library()
     _need_device(q, k_cache, v_cache, block_table, context_lens)
     num_seqs, Hq, d = q.shape
-    num_blocks, block_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    num_blocks, block_size, Hkv = _cache_dims(k_cache, cache_dims)
     if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise TypeError("block_table and context_lens must be int32")
     max_blocks = block_table.shape[1]

@@ -79,6 +79,22 @@ attn_status_t check_fwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, floa
   return ATTN_OK;
 }
 
+// Layout identity of a paged cache ("Failure modes": page-table mismatch):
+// the strides (elements) must place the block_size x Hkv rows of d values
+// of a page without overlap, 16-byte aligned, either token-major
+// ([block, slot, head, d]: head_stride >= d, token_stride >= Hkv *
+// head_stride) or head-major ([block, head, slot, d]: token_stride >= d,
+// head_stride >= block_size * token_stride), with pages not overlapping.
+bool page_layout_ok(int d, int Hkv, int block_size, int64_t block_stride, int64_t token_stride,
+                    int64_t head_stride) {
+  if (head_stride % 8 || token_stride % 8 || block_stride % 8) return false;
+  if (head_stride >= d && token_stride >= (int64_t)Hkv * head_stride)
+    return block_stride >= (int64_t)block_size * token_stride;
+  if (token_stride >= d && head_stride >= (int64_t)block_size * token_stride)
+    return block_stride >= (int64_t)Hkv * head_stride;
+  return false;
+}
+
 // Window sides as the kernels take them: -1 (no limit) becomes kUnbounded.
 bool window_sides(int window_left, int window_right, int* left, int* right) {
   if (window_left < -1 || window_right < -1) return false;
@@ -347,9 +363,7 @@ attn_status_t attn_prefill_paged(const void* Q, const void* K_cache, const void*
                 block_size);
   if ((long long)max_blocks_per_seq * block_size >= (1LL << 31))
     return fail(ATTN_ERR_INVALID_ARG, "block table capacity exceeds 2^31 tokens");
-  if (head_stride < d || token_stride < (int64_t)Hkv * head_stride ||
-      block_stride < (int64_t)block_size * token_stride || head_stride % 8 || token_stride % 8 ||
-      block_stride % 8)
+  if (!page_layout_ok(d, Hkv, block_size, block_stride, token_stride, head_stride))
     return fail(ATTN_ERR_INVALID_ARG,
                 "cache strides inconsistent with block_size=%d Hkv=%d d=%d "
                 "(block=%lld token=%lld head=%lld)",
@@ -369,13 +383,7 @@ attn_status_t attn_prefill_paged(const void* Q, const void* K_cache, const void*
   a.seq.max_blocks = max_blocks_per_seq;
   a.seq.num_blocks = num_blocks;
   a.seq.block_size = block_size;
-  // Division of 31-bit keys by block_size: m = floor(2^(31+l) / bs) + 1 with
-  // l = ceil(log2 bs) gives key / bs = (key * m) >> (31 + l) exactly, since
-  // the error key * (m - 2^(31+l)/bs) / 2^(31+l) stays below 1/bs; m < 2^32.
-  int l = 0;
-  while ((1LL << l) < block_size) ++l;
-  a.seq.page_magic = (unsigned)((1ULL << (31 + l)) / (unsigned long long)block_size + 1);
-  a.seq.page_shift = 31 + l;
+  eta::page_magic(block_size, a.seq.page_magic, a.seq.page_shift);
   a.seq.block_stride = block_stride;
   a.seq.token_stride = token_stride;
   a.seq.head_stride = head_stride;
@@ -500,9 +508,7 @@ attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* 
     return fail(ATTN_ERR_INVALID_ARG, "scale must be positive and finite");
   // Layout identity ("Failure modes": page-table mismatch): the strides must
   // describe disjoint, 16-byte aligned rows.
-  if (head_stride < d || token_stride < (int64_t)Hkv * head_stride ||
-      block_stride < (int64_t)block_size * token_stride || head_stride % 8 || token_stride % 8 ||
-      block_stride % 8)
+  if (!page_layout_ok(d, Hkv, block_size, block_stride, token_stride, head_stride))
     return fail(ATTN_ERR_INVALID_ARG,
                 "cache strides inconsistent with block_size=%d Hkv=%d d=%d "
                 "(block=%lld token=%lld head=%lld)",

@@ -56,41 +56,46 @@ constexpr int kMaxChunk = 4064;
 #define ETA_DECODE_WG_WAVES 4
 #endif
 
-// Work order of the split kernels.  Work item i = (sequence s, chunk c)
-// enumerates the live chunks only, sequence by sequence (c < ceil(ctx_s /
-// chunk_tokens)); a wave's slot id = i * Hkv + g.  The grid is sized for the
+// Work order of the split kernels.  Work items enumerate the live chunks
+// only: first every sequence's full chunks (sequence by sequence), then the
+// shorter last chunks of the sequences whose context is not a multiple of
+// chunk_tokens, so the short items fill the end of the launch (longest work
+// first).  A wave's slot id = item * Hkv + g.  The grid is sized for the
 // largest possible count, so the live work is dispatched first and the
 // surplus slots at the end exit at once (measured faster than a grid with
 // dead slots interleaved through it).  The wave finds its sequence by an
-// inclusive scan of the chunk counts of 64 sequences at a time.  Returns g
-// and sets s = -1 for a surplus slot.
+// inclusive scan of the per-sequence counts of 64 sequences at a time.
+// Returns g and sets s = -1 for a surplus slot.
 __device__ __forceinline__ int live_item(int slot, int Hkv, const int* __restrict__ ctx_lens,
                                          int num_seqs, int max_context, int chunk_tokens,
                                          int lane, int& s_out, int& chunk_out) {
   int item = slot / Hkv;
   const int g = slot % Hkv;
   int s = -1, chunk = 0;
-  for (int base = 0; base < num_seqs; base += 64) {
-    const int sq = base + lane;
-    int nc = 0;
-    if (sq < num_seqs) {
-      const int c = min(ctx_lens[sq], max_context);
-      nc = c > 0 ? (c + chunk_tokens - 1) / chunk_tokens : 0;
-    }
-    int incl = nc;
+  for (int pass = 0; pass < 2 && s < 0; ++pass) {
+    for (int base = 0; base < num_seqs; base += 64) {
+      const int sq = base + lane;
+      int nc = 0, full = 0;
+      if (sq < num_seqs) {
+        const int c = min(ctx_lens[sq], max_context);
+        full = c > 0 ? c / chunk_tokens : 0;
+        nc = pass == 0 ? full : (c > 0 && c % chunk_tokens != 0 ? 1 : 0);
+      }
+      int incl = nc;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += t;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
+      }
+      const unsigned long long hit = __ballot(incl > item);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        s = base + l;
+        chunk = pass == 0 ? item - (__shfl(incl, l, 64) - __shfl(nc, l, 64)) : __shfl(full, l, 64);
+        break;
+      }
+      item -= __shfl(incl, 63, 64);
     }
-    const unsigned long long hit = __ballot(incl > item);
-    if (hit) {
-      const int l = __builtin_ctzll(hit);
-      s = base + l;
-      chunk = item - (__shfl(incl, l, 64) - __shfl(nc, l, 64));
-      break;
-    }
-    item -= __shfl(incl, 63, 64);
   }
   s_out = __builtin_amdgcn_readfirstlane(s);
   chunk_out = __builtin_amdgcn_readfirstlane(chunk);
@@ -106,7 +111,7 @@ void decode_split_paged_kernel(
     float* __restrict__ part_o, float* __restrict__ part_ml, int num_seqs, int Hq, int Hkv,
     int G, int block_size, int num_blocks, int max_blocks, int max_context, int chunk_tokens,
     int n_chunks_max, long long block_stride, long long token_stride, long long head_stride,
-    float scale_log2) {
+    float scale_log2, unsigned page_magic, int page_shift) {
   constexpr int KS = D / 32;          // k-steps of S^T = K Q^T (32 d each)
   constexpr int NB = D / 16;          // 16-row blocks of o^T
   constexpr int CH = D / 8;           // 16-byte chunks per row
@@ -143,11 +148,10 @@ void decode_split_paged_kernel(
 
   const int* bt = block_table + (size_t)s * max_blocks;
   const int ts2 = (int)(token_stride * 2);  // bytes between tokens
-  const int hs2 = (int)(head_stride * 2);
   // Per-lane byte offsets inside a 16-token group: the K row of token qc
   // (A operand, d = 32 ks + 8 g4 + e) and this lane's V chunk.
-  const int koff = qc * ts2 + g * hs2 + 16 * g4;
-  const int voff = (lane / CH) * ts2 + g * hs2 + (lane % CH) * 16;
+  const int koff = qc * ts2 + 16 * g4;
+  const int voff = (lane / CH) * ts2 + (lane % CH) * 16;
 
   // The chunk's block-table entries (up to 4 * 64 logical pages, enough for
   // kMaxChunk tokens), one per lane of bt_r[i], loaded once: page lookups
@@ -178,11 +182,13 @@ void decode_split_paged_kernel(
     live = live < 0 ? 0 : live;
     long long base = 0;
     if (live > 0) {
-      const int logical = pos0 / block_size;
+      const int logical = (int)(((unsigned long long)(unsigned)pos0 * page_magic) >> page_shift);
       const int slot0 = pos0 - logical * block_size;
       const int ph = page_of(logical);
       if (ph < 0 || ph >= num_blocks) live = 0;
-      else base = (long long)ph * block_stride + (long long)slot0 * token_stride;
+      else
+        base = (long long)ph * block_stride + (long long)slot0 * token_stride +
+               (long long)g * head_stride;
     }
     live = __builtin_amdgcn_readfirstlane(live);
     const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)base);
@@ -594,13 +600,26 @@ hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t
     // beyond the live work exit at once (and come last in launch order).
     const long long slots = (long long)units * a.num_seqs;
     dim3 grid((unsigned)((slots + wg_waves - 1) / wg_waves));
-    auto kern = paged ? decode_split_paged_kernel<D> : decode_split_generic_kernel<D>;
-    hipLaunchKernelGGL(kern, grid, dim3(64 * wg_waves), 0, stream,
-                       (const __bf16*)a.Q, (const __bf16*)a.K_cache, (const __bf16*)a.V_cache,
-                       a.block_table, a.context_lens, part_o, part_ml, a.num_seqs, a.Hq, a.Hkv,
-                       a.Hq / a.Hkv, a.block_size, a.num_blocks, a.max_blocks_per_seq,
-                       a.max_context, p.chunk_tokens, p.n_chunks_max, (long long)a.block_stride, (long long)a.token_stride,
-                       (long long)a.head_stride, a.scale * kLog2e);
+    if (paged) {
+      unsigned magic;
+      int shift;
+      page_magic(a.block_size, magic, shift);
+      hipLaunchKernelGGL(decode_split_paged_kernel<D>, grid, dim3(64 * wg_waves), 0, stream,
+                         (const __bf16*)a.Q, (const __bf16*)a.K_cache, (const __bf16*)a.V_cache,
+                         a.block_table, a.context_lens, part_o, part_ml, a.num_seqs, a.Hq, a.Hkv,
+                         a.Hq / a.Hkv, a.block_size, a.num_blocks, a.max_blocks_per_seq,
+                         a.max_context, p.chunk_tokens, p.n_chunks_max,
+                         (long long)a.block_stride, (long long)a.token_stride,
+                         (long long)a.head_stride, a.scale * kLog2e, magic, shift);
+    } else {
+      hipLaunchKernelGGL(decode_split_generic_kernel<D>, grid, dim3(64 * wg_waves), 0, stream,
+                         (const __bf16*)a.Q, (const __bf16*)a.K_cache, (const __bf16*)a.V_cache,
+                         a.block_table, a.context_lens, part_o, part_ml, a.num_seqs, a.Hq, a.Hkv,
+                         a.Hq / a.Hkv, a.block_size, a.num_blocks, a.max_blocks_per_seq,
+                         a.max_context, p.chunk_tokens, p.n_chunks_max,
+                         (long long)a.block_stride, (long long)a.token_stride,
+                         (long long)a.head_stride, a.scale * kLog2e);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -77,6 +77,17 @@ __host__ __device__ inline void band_tiles(bool band, int q0, int rows, int Nq, 
   }
 }
 
+// Division of 31-bit token positions by a page size bs without a divide:
+// with l = ceil(log2 bs) and m = floor(2^(31+l) / bs) + 1, pos / bs ==
+// (pos * m) >> (31 + l) for every 0 <= pos < 2^31 (the error
+// pos * (m - 2^(31+l) / bs) / 2^(31+l) stays below 1 / bs), and m < 2^32.
+inline void page_magic(int bs, unsigned& magic, int& shift) {
+  int l = 0;
+  while ((1LL << l) < bs) ++l;
+  magic = (unsigned)((1ULL << (31 + l)) / (unsigned long long)bs + 1);
+  shift = 31 + l;
+}
+
 // Key-tile width of the bf16 forward for head dimension d.
 inline int fwd_tile_keys(int d) { return d == 128 ? 32 : 64; }
 

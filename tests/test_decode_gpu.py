@@ -229,3 +229,23 @@ def test_paged_gqa_decode_64seq_full_size_sampled(gpu):
                                         to64(vv).transpose(1, 0, 2)[None], scale, False)
         check_out(to64(o[s]), o_ref[0, :, 0], "bf16", what=f"seq {s}")
         check_lse(to64(lse[s]), lse_ref[0, :, 0], "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_head_major_page_layout(gpu, d):
+    """Pages stored head-major ([block, head, slot, d], each KV head's 16
+    rows contiguous) through the stride arguments: same result as the
+    token-major cache it was permuted from."""
+    w = workloads.decode(num_seqs=5, Hq=16, Hkv=4, d=d, ctx_lo=1, ctx_hi=700, dtype="bf16",
+                         seed=30 + d, poison_tail=True)
+    nb, bs, hkv, _ = w["k_cache"].shape
+    kh = w["k_cache"].permute(0, 2, 1, 3).contiguous()
+    vh = w["v_cache"].permute(0, 2, 1, 3).contiguous()
+    g = _to_gpu(w, gpu)
+    o, lse = attn.attn_decode_paged(g["q"], kh.to(gpu), vh.to(gpu), g["block_table"],
+                                    g["context_lens"], 0.1, w["max_context"], chunk_tokens=64,
+                                    strides=(hkv * bs * d, d, bs * d), cache_dims=(nb, bs, hkv))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _oracle(w, 0.1)
+    check_out(to64(o.cpu()), o_ref, "bf16")
+    check_lse(to64(lse.cpu()), lse_ref, "bf16")

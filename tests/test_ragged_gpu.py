@@ -222,3 +222,21 @@ def test_varlen_bench_shape_sampled(gpu):
         o_ref, lse_ref = oracle.forward(qs, kk, vv, vw["scale"], False, mask=vis)
         check_out(to64(o[torch.as_tensor(cu[s] + rows)]).transpose(1, 0, 2), o_ref[0], "bf16")
         check_lse(to64(lse[:, torch.as_tensor(cu[s] + rows)]), lse_ref[0], "bf16")
+
+
+def test_prefill_paged_head_major_layout(gpu):
+    """The paged prefill through a head-major cache ([block, head, slot, d])
+    given by strides equals the oracle on the token-major original."""
+    w = workloads.paged_prefill([30, 140], [300, 140], 8, 2, 128, block_size=32, seed=31,
+                                poison=True)
+    nb, bs, hkv, d = w["k_cache"].shape
+    kh = w["k_cache"].permute(0, 2, 1, 3).contiguous()
+    vh = w["v_cache"].permute(0, 2, 1, 3).contiguous()
+    o, lse = attn.attn_prefill_paged(w["q"].to(gpu), kh.to(gpu), vh.to(gpu),
+                                     w["block_table"].to(gpu), w["cu_q"].to(gpu),
+                                     w["seqlens_k"].to(gpu), w["max_q"], 0.09, -1, 0,
+                                     strides=(hkv * bs * d, d, bs * d), cache_dims=(nb, bs, hkv))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _paged_ref(w, 0.09, (-1, 0))
+    check_out(to64(o.cpu()), o_ref, "bf16")
+    check_lse(to64(lse.cpu()), lse_ref, "bf16")
