@@ -255,10 +255,13 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_con
  *   chunk_tokens context chunk per parallel work item, a positive multiple
  *                of 32 up to 4064, or 0 to let the library choose.
  *   Hq % Hkv == 0 and Hq / Hkv <= 16; d in {64, 128}; dtype must be BF16;
- *   block_size >= 1; the strides must describe non-overlapping rows:
- *   head_stride >= d, token_stride >= Hkv*head_stride,
- *   block_stride >= block_size*token_stride, all multiples of 8, and
- *   block_stride < 2^30 (else ATTN_ERR_UNSUPPORTED).
+ *   block_size >= 1; the strides must describe non-overlapping rows, all
+ *   multiples of 8, in one of two page layouts:
+ *     token-major [block, slot, head, d]: head_stride >= d,
+ *       token_stride >= Hkv*head_stride, block_stride >= block_size*token_stride;
+ *     head-major [block, head, slot, d]: token_stride >= d,
+ *       head_stride >= block_size*token_stride, block_stride >= Hkv*head_stride;
+ *   and block_stride < 2^30 (else ATTN_ERR_UNSUPPORTED).
  *   workspace    device scratch of at least
  *                attn_decode_paged_workspace_size(...) bytes, 16-byte aligned.
  */
