@@ -14,9 +14,11 @@ Each call is bracketed by HIP events recorded on the stream the library
 launches on (torch's current stream); the K timed steps are bracketed by a
 device synchronisation on both sides.  Rank 0 prints one JSON line.
 
-After the timed steps, the entry points beyond the hot path are timed the
-same way in a loop of their own (K calls each, after W warm-up calls), so
-they do not change the conditions the step is measured under:
+After the timed steps, the other forward configurations (d = 64: B=4, H=16,
+N=2048 causal; the headline shape non-causal) and the entry points beyond the
+hot path are timed the same way in a loop of their own (K calls each, after W
+warm-up calls), so they do not change the conditions the step is measured
+under:
   * the 4-head variant of (1) through the key split;
   * a packed ragged causal prefill (16 sequences of 512..8192 tokens, GQA
     32/8, d=128);
@@ -200,7 +202,22 @@ def main():
                       workspace=bws, stream=stream)
         if e: e[3].record(stream)
 
+    # The other forward configurations: d = 64 (B=4, H=16, N=2048, causal)
+    # and the headline shape without the mask.
+    c2 = workloads.WORKLOADS["causal_bf16_b4_h16_n2048_d64"]
+    c2q, c2k, c2v = workloads.prefill(c2["B"], c2["H"], c2["Hkv"], c2["Nq"], c2["Nk"], c2["d"],
+                                      dtype="bf16", seed=c2["seed"], device=str(dev))
+    c2o = torch.empty_like(c2q)
+    c2lse = torch.empty((c2["B"], c2["H"], c2["Nq"]), dtype=torch.float32, device=dev)
+    c2_flops = 4.0 * c2["B"] * c2["H"] * c2["Nq"] * c2["Nk"] * c2["d"] / 2.0
+    nc = workloads.WORKLOADS["noncausal_bf16_b1_h32_n8192_d128"]
+    nc_flops = 4.0 * nc["B"] * nc["H"] * nc["Nq"] * nc["Nk"] * nc["d"]
+
     extras = [
+        ("fwd_d64", c2_flops, lambda: attn.attn_fwd(c2q, c2k, c2v, c2["scale"], True, out=c2o,
+                                                    lse=c2lse, stream=stream)),
+        ("fwd_noncausal", nc_flops, lambda: attn.attn_fwd(q, k, v, nc["scale"], False, out=o,
+                                                          lse=lse, stream=stream)),
         ("fwd_small_grid", split_flops, lambda: attn.attn_fwd_splitkv(
             sq, sk, sv, sw["scale"], -1, 0, out=so, lse=slse, workspace=sws, stream=stream)),
         ("varlen", varlen_flops, lambda: attn.attn_fwd_varlen(
@@ -324,6 +341,9 @@ def main():
                                **{k: round(v[1], 4) for k, v in extra.items()}},
     }
     for name, workload, note in [
+            ("fwd_d64", "causal_bf16_b4_h16_n2048_d64 (attn_fwd)", "d = 64, 64-key tiles"),
+            ("fwd_noncausal", "noncausal_bf16_b1_h32_n8192_d128 (attn_fwd)",
+             "the headline shape without the mask"),
             ("varlen", "varlen_causal_bf16_s16_h32_hkv8_d128 (attn_fwd_varlen)",
              f"{len(vlens)} packed sequences, {sum(vlens)} tokens"),
             ("paged_prefill", "paged_prefill_causal_bf16_s16_hq32_hkv8_d128 (attn_prefill_paged)",
