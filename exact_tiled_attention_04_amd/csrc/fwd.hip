@@ -119,7 +119,17 @@ __device__ __forceinline__ void grid_tile(int wg, int n_qtiles, int B, int H, in
   const int P = B * Hkv;
   if ((P & 7) == 0) {
     const int G = H / Hkv;
-    const int x = wg & 7, k = wg >> 3;
+    const int x = wg & 7;
+    int k = wg >> 3;
+    if (!PAIR_MAJOR) {
+      // Every other full round of 32 workgroups on the XCD (one per CU) runs
+      // in reverse, so the workgroups that meet on a CU at the start of the
+      // launch pair heavier with lighter query tiles (measured +2.7% on
+      // 4 x 16 heads x 2k causal, where the whole grid is resident at once).
+      const int per_xcd = n_qtiles * (P >> 3) * G;
+      const int r = k >> 5;
+      if ((r & 1) && (r << 5) + 31 < per_xcd) k = (r << 5) + 31 - (k & 31);
+    }
     const int hg = k % G, kk = k / G;
     const int per = P >> 3;
     const int pp = PAIR_MAJOR ? kk / n_qtiles : kk % per;
