@@ -25,8 +25,12 @@
 //     and the accumulator is rescaled only when the reference max moves;
 //   * grid = batch x head x query tile ("Work partitioning in
 //     FlashAttention-2": parallel over the sequence), causal tiles heaviest
-//     first, consecutive workgroups on different heads so that each XCD's L2
-//     serves a fixed subset of heads.
+//     first, each (batch, KV head) pair owned by one XCD so that its L2
+//     serves the heads that share the pair's K and V (grid_tile);
+//   * one kernel, four row modes: dense [B, H, N, d]; packed ragged
+//     sequences; ragged queries over a paged K/V cache; dense rows visiting
+//     only the blocks of a sparse block index.  Only the addressing, the
+//     per-sequence lengths and the visited tiles differ between them.
 #include "common.hpp"
 #include "kernels.hpp"
 
