@@ -593,7 +593,7 @@ int attn_plan_describe(int phase, int B, int H, int Hkv, int Nq, int Nk, int d, 
     n = snprintf(tmp, sizeof(tmp),
                  "phase=bwd kernels=bwd_pre+bwd_dkdv_mfma32x32x16+bwd_dq_mfma32x32x16 d=%d "
                  "causal=%d dkdv: key_tile=128 (4 waves x 32 keys, K in LDS) query_tile=32 grid=%lld "
-                 "(B*Hkv*ceil(Nk/128)); dq: query_tile=128 key_tile=64 grid=%lld "
+                 "(B*Hkv*ceil(Nk/128)); dq: query_tile=128 key_tile=32 grid=%lld "
                  "(B*H*ceil(Nq/128)); deterministic (no atomics)",
                  d, causal ? 1 : 0, (long long)B * Hkv * ((Nk + 127) / 128),
                  (long long)B * H * ((Nq + 127) / 128));
