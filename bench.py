@@ -62,6 +62,10 @@ def _parse():
                          "can be scaled against a kernel of known traffic")
     ap.add_argument("--cpu-heads", type=int, default=24,
                     help="heads of the forward workload the oracle is timed on")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line, time a sweep of shapes (batch, lengths, "
+                         "heads, head dimension, masks, cache block size) and print one JSON "
+                         "line per shape")
     return ap.parse_args()
 
 
@@ -103,6 +107,8 @@ def main():
     attn.load_library()  # fails loudly when the HIP library is missing
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
+    if args.sweep:
+        return sweep(args, dev, stream)
     if args.copy_calibration:
         # 512 MiB read + 512 MiB written by one copy kernel.
         src = torch.ones(256 << 20, dtype=torch.bfloat16, device=dev)
@@ -256,7 +262,7 @@ def main():
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
         ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-        extra[name] = (sum(ms) / len(ms), med(ms), flops)
+        extra[name] = (sum(ms) / len(ms), med(ms), flops, ms)
 
     fwd_ms = [ev[0].elapsed_time(ev[1]) for ev in events]
     dec_ms = [ev[1].elapsed_time(ev[2]) for ev in events]
@@ -339,6 +345,14 @@ def main():
         "per_call_ms_median": {"fwd": round(med(fwd_ms), 4), "decode": round(med(dec_ms), 4),
                                "bwd": round(med(bwd_ms), 4),
                                **{k: round(v[1], 4) for k, v in extra.items()}},
+        # Tail behaviour ("Benchmarking method": medians plus tails), kernel
+        # launches and temporary (workspace) bytes per call.
+        "per_call_ms_tail": {"fwd": _tail(fwd_ms), "decode": _tail(dec_ms), "bwd": _tail(bwd_ms),
+                             **{k: _tail(v[3]) for k, v in extra.items()}},
+        "launches_and_temporary_bytes": {
+            "fwd": [1, 0], "decode": [2, dws.numel()], "bwd": [3, bws.numel()],
+            "fwd_small_grid": [2, sws_bytes], "varlen": [1, 0], "paged_prefill": [1, 0],
+            "block_sparse": [1, 0]},
     }
     for name, workload, note in [
             ("fwd_d64", "causal_bf16_b4_h16_n2048_d64 (attn_fwd)", "d = 64, 64-key tiles"),
@@ -350,7 +364,7 @@ def main():
              f"{sum(pp['q_lens'])} new tokens over {sum(pp['k_lens'])} cached"),
             ("block_sparse", "block_sparse_causal_bf16_b1_h32_n8192_d128 (attn_fwd_block_sparse)",
              f"visible pairs {100 * sparse_density:.1f}% of causal")]:
-        avg, _, flops = extra[name]
+        avg, _, flops, _ = extra[name]
         tf = flops / (avg * 1e-3) / 1e12
         result[name] = {"workload": workload, "value": round(tf, 2), "unit": "TFLOP/s",
                         "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -360,6 +374,115 @@ def main():
         result["cpu_baseline"] = cpu_baseline(q, k, v, fw, args.cpu_heads)
     print(json.dumps(result))
     return 0
+
+
+def _time_calls(call, stream, calls, warmup):
+    """Per-call milliseconds of `calls` back-to-back calls after `warmup`."""
+    import torch
+    for _ in range(warmup):
+        call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(calls):
+        call()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(calls)]
+
+
+def sweep(args, dev, stream):
+    """The shape space of "Modern attention kernels", "Benchmarking method":
+    batch, query and key length, heads and KV heads, head dimension, causal /
+    local / block-sparse masks, cache block size.  One JSON line per shape
+    with TFLOP/s (visible pairs x 4 d) or KV GB/s, median and tail."""
+    import torch
+    from exact_tiled_attention_04_amd import attn, workloads
+
+    calls, warm = max(args.steps, 5), max(args.warmup, 2)
+
+    def emit(kind, shape, ms, work, unit):
+        t = _tail(ms)
+        rate = work / (t["p50"] * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        print(json.dumps({"sweep": kind, **shape, "value": round(rate, 1), "unit": unit,
+                          "ms": t}), flush=True)
+
+    # Forward: batch, length, heads / KV heads, head dimension, mask.
+    for B, H, Hkv, N, d in [(1, 32, 32, 8192, 128), (1, 32, 8, 8192, 128), (2, 16, 16, 4096, 128),
+                            (8, 16, 16, 2048, 128), (4, 16, 16, 2048, 64), (16, 16, 4, 1024, 64),
+                            (1, 8, 8, 16384, 128), (32, 32, 8, 512, 128)]:
+        q, k, v = workloads.prefill(B, H, Hkv, N, N, d, seed=1, device=str(dev))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        for mask, wl, wr in [("causal", -1, 0), ("none", -1, -1), ("window1024", 1023, 0)]:
+            if mask == "window1024" and N <= 1024:
+                continue
+            call = lambda: attn.attn_fwd_local(q, k, v, 1 / math.sqrt(d), wl, wr, out=o, lse=lse,  # noqa: E731
+                                               stream=stream)
+            ms = _time_calls(call, stream, calls, warm)
+            if mask == "causal":
+                pairs = N * (N + 1) / 2
+            elif mask == "none":
+                pairs = N * N
+            else:
+                pairs = sum(min(i + 1, wl + 1) for i in range(N))
+            emit("fwd", {"B": B, "H": H, "Hkv": Hkv, "N": N, "d": d, "mask": mask}, ms,
+                 4.0 * d * B * H * pairs, "TFLOP/s")
+        del q, k, v, o, lse
+    # Rectangular (a chunk of queries at the end of a longer context), plain
+    # and through the key split (which needs a workspace, so only
+    # attn_fwd_splitkv takes it).
+    for Nq, Nk in [(512, 8192), (2048, 16384)]:
+        q, k, v = workloads.prefill(1, 32, 8, Nq, Nk, 128, seed=2, device=str(dev))
+        pairs = Nq * (Nk - Nq) + Nq * (Nq + 1) / 2
+        ms = _time_calls(lambda: attn.attn_fwd(q, k, v, 1 / math.sqrt(128), True, stream=stream),
+                         stream, calls, warm)
+        emit("fwd", {"B": 1, "H": 32, "Hkv": 8, "Nq": Nq, "Nk": Nk, "d": 128, "mask": "causal"},
+             ms, 4.0 * 128 * 32 * pairs, "TFLOP/s")
+        need = attn.attn_fwd_splitkv_workspace_size(1, 32, Nq, Nk, 128, -1, 0, 0)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        ms = _time_calls(lambda: attn.attn_fwd_splitkv(q, k, v, 1 / math.sqrt(128), -1, 0,  # noqa: E731
+                                                       workspace=ws, stream=stream),
+                         stream, calls, warm)
+        emit("fwd_splitkv", {"B": 1, "H": 32, "Hkv": 8, "Nq": Nq, "Nk": Nk, "d": 128,
+                             "mask": "causal", "split": need > 0}, ms,
+             4.0 * 128 * 32 * pairs, "TFLOP/s")
+    # Decode: sequences, context length, GQA group, cache block size.
+    for S, Hq, Hkv, lo, hi, bs in [(64, 32, 8, 4096, 32768, 16), (64, 32, 8, 4096, 32768, 32),
+                                   (16, 32, 8, 32768, 65536, 16), (256, 32, 8, 1024, 4096, 16),
+                                   (64, 64, 8, 8192, 16384, 16), (128, 16, 16, 2048, 8192, 16)]:
+        w = workloads.decode(num_seqs=S, Hq=Hq, Hkv=Hkv, d=128, ctx_lo=lo, ctx_hi=hi,
+                             block_size=bs, max_blocks_per_seq=(hi + bs - 1) // bs,
+                             dtype="bf16", seed=3, device=str(dev))
+        bt, cl = w["block_table"].to(dev), w["context_lens"].to(dev)
+        ws = torch.empty(max(attn.attn_decode_paged_workspace_size(S, Hq, 128, hi, 0), 16),
+                         dtype=torch.uint8, device=dev)
+        call = lambda: attn.attn_decode_paged(w["q"], w["k_cache"], w["v_cache"], bt, cl,  # noqa: E731
+                                              1 / math.sqrt(128), hi, workspace=ws, stream=stream)
+        ms = _time_calls(call, stream, calls, warm)
+        emit("decode", {"seqs": S, "Hq": Hq, "Hkv": Hkv, "ctx": [lo, hi], "block_size": bs}, ms,
+             2.0 * int(w["context_lens"].sum()) * Hkv * 128 * 2, "GB/s")
+        del w, bt, cl, ws
+    # Backward.
+    for B, H, Hkv, N, d in [(2, 16, 16, 4096, 128), (1, 32, 8, 8192, 128), (4, 16, 16, 2048, 64)]:
+        q, k, v, do = workloads.backward(B, H, Hkv, N, N, d, seed=4, device=str(dev))
+        o, lse = attn.attn_fwd(q, k, v, 1 / math.sqrt(d), True)
+        ws = torch.empty(attn.attn_bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device=dev)
+        call = lambda: attn.attn_bwd(q, k, v, o, do, lse, 1 / math.sqrt(d), True, workspace=ws,  # noqa: E731
+                                     stream=stream)
+        ms = _time_calls(call, stream, calls, warm)
+        emit("bwd", {"B": B, "H": H, "Hkv": Hkv, "N": N, "d": d, "mask": "causal"}, ms,
+             10.0 * d * B * H * N * (N + 1) / 2, "TFLOP/s")
+        del q, k, v, do, o, lse, ws
+    return 0
+
+
+def _tail(ms):
+    """p10 / median / p90 / max of per-call milliseconds."""
+    v = sorted(ms)
+    pick = lambda q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]  # noqa: E731
+    return {"p10": round(pick(0.1), 4), "p50": round(pick(0.5), 4), "p90": round(pick(0.9), 4),
+            "max": round(v[-1], 4)}
 
 
 def _sparse_pairs(row_ptr, col_idx, block=128):
