@@ -43,26 +43,12 @@ namespace eta {
 namespace {
 
 constexpr int kBK = 128;  // keys per dK/dV workgroup (32 per wave)
-// dK/dV kernel shape: K of the wave's keys in LDS (else registers), query
-// tiles of 32 rows (or 64), two waves per SIMD (or one).
-#ifndef ETA_BWD_K_LDS
-#define ETA_BWD_K_LDS 1
-#endif
-#ifndef ETA_BWD_BQ
-#define ETA_BWD_BQ 32
-#endif
-constexpr int kBQ = ETA_BWD_BQ;  // queries per dK/dV inner tile (32 or 64)
-constexpr int kQB = kBQ / 32;     // 32-row query blocks per inner tile
+constexpr int kBQ = 32;   // queries per dK/dV inner tile
+constexpr int kQB = kBQ / 32;  // 32-row query blocks per inner tile
 constexpr int kBC = 32;   // keys per dQ inner tile (measured 1.5% faster than 64)
 constexpr int kKB = kBC / 32;  // 32-key blocks per dQ tile
 constexpr int kBR = 128;  // queries per dQ workgroup
 
-#ifndef ETA_BWD_KV_WAVES_PER_EU
-#define ETA_BWD_KV_WAVES_PER_EU 2
-#endif
-#ifndef ETA_BWD_Q_WAVES_PER_EU
-#define ETA_BWD_Q_WAVES_PER_EU 2
-#endif
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ O,
@@ -97,7 +83,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 // ----------------------------------------------------------------- dK, dV
 
 template <int D, bool BAND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETA_BWD_KV_WAVES_PER_EU)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ LSE2, const float* __restrict__ Dsum,
@@ -116,11 +102,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   __shared__ __attribute__((aligned(16))) char sm0[BUF];
   __shared__ __attribute__((aligned(16))) char sm1[BUF];
-#if ETA_BWD_K_LDS
   // Each wave's 32 K rows, swizzled like the Q tiles (B operand of S = Q K^T
   // read from LDS instead of held in 32 registers).
   __shared__ __attribute__((aligned(16))) char ksm[4][32 * ROW];
-#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -143,7 +127,6 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int jw = j0 + 32 * wave + li;
   const buf_rsrc krs = make_rsrc(K + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
   const buf_rsrc vrs = make_rsrc(V + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
-#if ETA_BWD_K_LDS
   const char* Kw = ksm[wave];
   {
     // Direct copies of the wave's 32 K rows: instruction it fills slots
@@ -160,14 +143,6 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     vf[ks] = __builtin_bit_cast(bf16x8, buf_load16(vrs, jw * ROW + (16 * ks + 8 * hh) * 2, 0));
-#else
-  bf16x8 kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(krs, jw * ROW + (16 * ks + 8 * hh) * 2, 0));
-    vf[ks] = __builtin_bit_cast(bf16x8, buf_load16(vrs, jw * ROW + (16 * ks + 8 * hh) * 2, 0));
-  }
-#endif
 
   // Query tiles that can see this key tile, for each head of the group:
   // query i (position i + off) sees key j iff j - win_right <= i + off <=
@@ -251,11 +226,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       const char* orow = Os + qb * 32 * ROW;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-#if ETA_BWD_K_LDS
         s = mfma32(*(const bf16x8*)(qrow + rofs[ks]), *(const bf16x8*)(Kw + rofs[ks]), s);
-#else
-        s = mfma32(*(const bf16x8*)(qrow + rofs[ks]), kf[ks], s);
-#endif
         dp = mfma32(*(const bf16x8*)(orow + rofs[ks]), vf[ks], dp);
       }
       // Lane (key jw, hh) register r holds query row q0 + 32 qb + 8 (r/4) + 4 hh + r%4.
@@ -339,7 +310,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // --------------------------------------------------------------------- dQ
 
 template <int D, bool BAND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETA_BWD_Q_WAVES_PER_EU)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                    const float* __restrict__ LSE2, const float* __restrict__ Dsum,
