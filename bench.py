@@ -219,7 +219,16 @@ def main():
     nc = workloads.WORKLOADS["noncausal_bf16_b1_h32_n8192_d128"]
     nc_flops = 4.0 * nc["B"] * nc["H"] * nc["Nq"] * nc["Nk"] * nc["d"]
 
+    # Context for the MFMA roofline: the vendor's bf16 GEMM (torch.matmul)
+    # on this GPU, timed the same way -- the sustained rate dense MFMA work
+    # gets under the chip's power limit.
+    ga = torch.randn(16384, 4096, device=dev, dtype=torch.bfloat16)
+    gb = torch.randn(4096, 16384, device=dev, dtype=torch.bfloat16)
+    gc = torch.empty(16384, 16384, device=dev, dtype=torch.bfloat16)
+    gemm_flops = 2.0 * 16384 * 16384 * 4096
+
     extras = [
+        ("vendor_gemm", gemm_flops, lambda: torch.matmul(ga, gb, out=gc)),
         ("fwd_d64", c2_flops, lambda: attn.attn_fwd(c2q, c2k, c2v, c2["scale"], True, out=c2o,
                                                     lse=c2lse, stream=stream)),
         ("fwd_noncausal", nc_flops, lambda: attn.attn_fwd(q, k, v, nc["scale"], False, out=o,
@@ -312,6 +321,7 @@ def main():
             "traffic": _traffic("fwd_bf16_kernel<D=128,band=causal,NW=4,BC=32>", fwd_src, None),
             "avg_launch_ms": round(fwd_avg, 4),
             "algorithmic_flop_per_launch": fwd_flops,
+            "vendor_bf16_gemm_tflops": round(gemm_flops / (extra["vendor_gemm"][0] * 1e-3) / 1e12, 1),
         },
         "decode": {
             "value": round(dec_gbs, 1),
@@ -349,6 +359,9 @@ def main():
         # launches and temporary (workspace) bytes per call.
         "per_call_ms_tail": {"fwd": _tail(fwd_ms), "decode": _tail(dec_ms), "bwd": _tail(bwd_ms),
                              **{k: _tail(v[3]) for k, v in extra.items()}},
+        "vendor_gemm": {"workload": "torch.matmul bf16 16384x16384x4096 (hipBLASLt)",
+                        "value": round(gemm_flops / (extra["vendor_gemm"][0] * 1e-3) / 1e12, 1),
+                        "unit": "TFLOP/s"},
         "launches_and_temporary_bytes": {
             "fwd": [1, 0], "decode": [2, dws.numel()], "bwd": [3, bws.numel()],
             "fwd_small_grid": [2, sws_bytes], "varlen": [1, 0], "paged_prefill": [1, 0],
