@@ -21,13 +21,15 @@
 //             that can see the keys (for every query head of the KV group)
 //             are copied straight into LDS, double-buffered.  Each wave forms
 //             S = Q K^T and dP = dO V^T with its keys along the lanes, then P
-//             and dS, and accumulates dV^T += dO^T P and dK^T += Q^T (scale
-//             dS) with the transposed operands read by ds_read_b64_tr_b16.
+//             and dS, and accumulates dV^T += dO^T P and dK^T += Q^T dS with
+//             the transposed operands read by ds_read_b64_tr_b16 (the
+//             softmax scale multiplies dK once, at the end).
 //   bwd_dq:   one workgroup per (batch, head, 128-query tile), four waves of
 //             32 queries, laid out like the forward: S^T = K Q^T and
 //             dP^T = V dO^T with the queries along the lanes, then
-//             dQ^T += K^T (scale dS)^T with K^T read transposed from the same
-//             LDS tile.  K/V tiles arrive by direct copies, double-buffered.
+//             dQ^T += K^T dS^T with K^T read transposed from the same LDS
+//             tile (scaled once at the end).  K/V tiles arrive by direct
+//             copies, double-buffered.
 // The split costs two extra products (S and dP are formed in both kernels)
 // and buys the removal of the fp32 dQ accumulator and its atomics.
 //
@@ -230,6 +232,16 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         dp = mfma32(*(const bf16x8*)(orow + rofs[ks]), vf[ks], dp);
       }
       // Lane (key jw, hh) register r holds query row q0 + 32 qb + 8 (r/4) + 4 hh + r%4.
+      // Band edges: scores outside the band become -inf (P = 0), in one
+      // block of selects taken only by the edge tiles.
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int pos = q0 + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3) + off;
+          if (jw > pos + win_right || jw < pos - win_left) s[r] = -INFINITY;
+        }
+      }
+      // dS without the softmax scale, which is applied once to dK at the end.
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int rloc = 32 * qb + 8 * r4 + 4 * hh;
@@ -238,13 +250,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[e]));
-          if (need_mask) {
-            const int pos = q0 + rloc + e + off;
-            if (jw > pos + win_right || jw < pos - win_left) p = 0.f;
-          }
+          const float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -l4[e]));
           s[r] = p;
-          dp[r] = p * (dp[r] - d4[e]) * scale;
+          dp[r] = p * (dp[r] - d4[e]);
         }
       }
 #pragma unroll
@@ -260,7 +268,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       }
     }
 
-    // dV^T += dO^T P and dK^T += Q^T (scale dS).
+    // dV^T += dO^T P and dK^T += Q^T dS.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -297,8 +305,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       for (int r4 = 0; r4 < 4; ++r4) {
         const int n = 32 * nb + 8 * r4 + 4 * hh;
         u32x2 a, c;
-        a[0] = pack_bf16x2(dk[nb][4 * r4 + 0], dk[nb][4 * r4 + 1]);
-        a[1] = pack_bf16x2(dk[nb][4 * r4 + 2], dk[nb][4 * r4 + 3]);
+        a[0] = pack_bf16x2(dk[nb][4 * r4 + 0] * scale, dk[nb][4 * r4 + 1] * scale);
+        a[1] = pack_bf16x2(dk[nb][4 * r4 + 2] * scale, dk[nb][4 * r4 + 3] * scale);
         c[0] = pack_bf16x2(dv[nb][4 * r4 + 0], dv[nb][4 * r4 + 1]);
         c[1] = pack_bf16x2(dv[nb][4 * r4 + 2], dv[nb][4 * r4 + 3]);
         *(u32x2*)(dkp + n) = a;
@@ -432,17 +440,23 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                        k0 < wave_row_lo + 31 + off - win_left));
       const int lim = BAND ? min(Nk - 1, qrow + off + win_right) : Nk - 1;
       const int lim_lo = BAND ? qrow + off - win_left : 0;
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key > lim || key < lim_lo) s[kb][r] = -INFINITY;
+          }
+      }
+      // dS without the softmax scale, which is applied once to dQ at the end.
       bf16x8 sb[kKB][2];
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -lse2));
-          if (need_mask) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key > lim || key < lim_lo) p = 0.f;
-          }
-          dp[kb][r] = p * (dp[kb][r] - dd) * scale;
+          const float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -lse2));
+          dp[kb][r] = p * (dp[kb][r] - dd);
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -453,7 +467,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           sb[kb][s2] = __builtin_bit_cast(bf16x8, w);
         }
       }
-      // dQ^T += K^T (scale dS)^T: K^T from the K tile by transpose reads.
+      // dQ^T += K^T dS^T: K^T from the K tile by transpose reads.
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -487,8 +501,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       for (int r4 = 0; r4 < 4; ++r4) {
         const int n = 32 * nb + 8 * r4 + 4 * hh;
         u32x2 w;
-        w[0] = pack_bf16x2(acc[nb][4 * r4 + 0], acc[nb][4 * r4 + 1]);
-        w[1] = pack_bf16x2(acc[nb][4 * r4 + 2], acc[nb][4 * r4 + 3]);
+        w[0] = pack_bf16x2(acc[nb][4 * r4 + 0] * scale, acc[nb][4 * r4 + 1] * scale);
+        w[1] = pack_bf16x2(acc[nb][4 * r4 + 2] * scale, acc[nb][4 * r4 + 3] * scale);
         *(u32x2*)(dst + n) = w;
       }
   }
