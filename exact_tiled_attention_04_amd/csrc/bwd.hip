@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 // ----------------------------------------------------------------- dK, dV
 
 template <int D, bool BAND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                      const float* __restrict__ LSE2, const float* __restrict__ Dsum,
@@ -188,9 +188,16 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     dk[nb] = f32x16{};
   }
 
-  auto load_tiles = [&](int itx, char* dst) {
-    const int h = g * G + itx / per_head;
-    const int q0 = (qt_begin + itx % per_head) * kBQ;
+  // Tiles run head by head of the group, query tiles in order within a
+  // head; (ld_head, ld_qt) is the next tile to copy, c_qt the tile computed.
+  int ld_head = 0, ld_qt = qt_begin, c_qt = qt_begin;
+  auto load_tiles = [&](char* dst) {
+    const int h = g * G + ld_head;
+    const int q0 = ld_qt * kBQ;
+    if (++ld_qt > qt_end) {
+      ld_qt = qt_begin;
+      ++ld_head;
+    }
     const size_t hb = ((size_t)b * H + h) * (size_t)Nq;
     const buf_rsrc qrs = make_rsrc(Q + hb * D, (unsigned)Nq * ROW);
     const buf_rsrc ors = make_rsrc(dO + hb * D, (unsigned)Nq * ROW);
@@ -211,8 +218,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   };
 
   auto step = [&](int itx, const char* cur, char* next) {
-    const int q0 = (qt_begin + itx % per_head) * kBQ;
-    if (itx + 1 < n_iter) load_tiles(itx + 1, next);
+    const int q0 = c_qt * kBQ;
+    c_qt = c_qt == qt_end ? qt_begin : c_qt + 1;
+    if (itx + 1 < n_iter) load_tiles(next);
     const char* Qs = cur;
     const char* Os = cur + QT;
     const float* lse2 = (const float*)(cur + STAT);
@@ -287,7 +295,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __syncthreads();
   };
 
-  if (n_iter > 0) load_tiles(0, sm0);
+  if (n_iter > 0) load_tiles(sm0);
   wait_vmem();
   __syncthreads();
   for (int itx = 0; itx < n_iter; itx += 2) {
