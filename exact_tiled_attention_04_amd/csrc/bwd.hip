@@ -51,6 +51,18 @@ constexpr int kBC = 32;   // keys per dQ inner tile (measured 1.5% faster than 6
 constexpr int kKB = kBC / 32;  // 32-key blocks per dQ tile
 constexpr int kBR = 128;  // queries per dQ workgroup
 
+// Launch order of both main kernels: heaviest causal tiles first.
+// Workgroups reach the eight XCDs round robin and, on an XCD, its 32 CUs in
+// turn, so in a launch whose grid is (nearly) all resident at once the CU
+// that takes workgroup k of a round of 256 also takes workgroup k of the next
+// round.  Every other full round runs in reverse CU order (same XCD), so a CU
+// pairs a heavy tile with a light one instead of two of similar weight.
+__device__ __forceinline__ int snake_order(int w, int n) {
+  const int r = w >> 8;
+  if ((r & 1) && ((r + 1) << 8) <= n) w = (r << 8) + ((31 - ((w & 255) >> 3)) << 3) + (w & 7);
+  return w;
+}
+
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ O,
@@ -117,8 +129,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int tr_c = lane & 3;
 
   const int BG = B * Hkv;
-  const int kt = blockIdx.x / BG;  // key tiles seen by the most queries first
-  const int bg = blockIdx.x % BG;
+  const int wg = snake_order(blockIdx.x, gridDim.x);
+  const int kt = wg / BG;  // key tiles seen by the most queries first
+  const int bg = wg % BG;
   const int b = bg / Hkv;
   const int g = bg % Hkv;
   const int G = H / Hkv;
@@ -352,8 +365,9 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int tr_c = lane & 3;
 
   const int BH = B * H;
-  const int qt = n_qtiles - 1 - blockIdx.x / BH;  // heavy query tiles first
-  const int bh = blockIdx.x % BH;
+  const int wg = snake_order(blockIdx.x, gridDim.x);
+  const int qt = n_qtiles - 1 - wg / BH;  // heavy query tiles first
+  const int bh = wg % BH;
   const int b = bh / H;
   const int h = bh % H;
   const int g = h / (H / Hkv);
