@@ -160,7 +160,7 @@ attn_status_t check_bwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, floa
 // FlashDecoding paragraph: split the key range and merge the partials).
 // When B*H*ceil(Nq/128) query tiles give fewer than two workgroups per CU,
 // each tile's key range is cut into equal parts sized for about four units
-// per CU in total (at least 256 keys each).  chunk_keys > 0 forces the part
+// per CU in total (at least 640 keys each).  chunk_keys > 0 forces the part
 // size.
 struct SplitPlan {
   int chunk_tiles = 0;
@@ -187,12 +187,14 @@ SplitPlan plan_fwd_split(int B, int H, int Nq, int Nk, int d, int left, int righ
       if (hi >= lo) work += hi - lo + 1;
     }
     work *= (long long)B * H;
-    // About four units per CU: parts of roughly 1000-1300 keys measured best
-    // on 4 heads x 8k causal (smaller parts pay more partial traffic and
-    // merge work, larger ones balance worse).
+    // About four units per CU, parts of at least 640 keys: shorter parts pay
+    // more partial traffic and merge work than they gain in balance (4 heads
+    // x 4k causal: 288-key parts 352-365 TFLOP/s, 640-key parts 433-446; the
+    // larger grids swept, 1-4 heads of 8k-32k, sit within 2% of their best
+    // part size).
     const long long target = 4LL * kNumCU;
     ct = (int)((work + target - 1) / target);
-    if (ct < 256 / bc) ct = 256 / bc;
+    if (ct < 640 / bc) ct = 640 / bc;
   }
   const int n_tiles = (Nk + bc - 1) / bc;
   int n_chunks = (n_tiles + ct - 1) / ct;
