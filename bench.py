@@ -389,11 +389,19 @@ def main():
     return 0
 
 
-def _time_calls(call, stream, calls, warmup):
-    """Per-call milliseconds of `calls` back-to-back calls after `warmup`."""
+def _time_calls(call, stream, calls, warmup, settle_s=0.03):
+    """Per-call milliseconds of `calls` back-to-back calls after `warmup`
+    calls and then at least `settle_s` seconds of further calls (an idle GPU
+    needs some tens of milliseconds of load before its clocks settle)."""
     import torch
     for _ in range(warmup):
         call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(4):
+            call()
+        torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
