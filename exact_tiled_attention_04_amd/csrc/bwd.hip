@@ -317,7 +317,17 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
 
   // Lane (key jw, hh) register r of block nb holds column 32 nb + 8 (r/4) + 4 hh + r%4.
-  if (jw < Nk) {
+  // At d = 64, after the last barrier the wave's K tile is idle: dK, then dV,
+  // go out through it as whole rows (the wave's own LDS operations run in
+  // order; measured 2% faster).  At d = 128 the staging needs a register
+  // the kernel does not have (it spilled, and 32 heads x 8k GQA ran 7%
+  // slower), so the C layout is stored directly.
+  if constexpr (D == 64) {
+    const int k_row0 = j0 + 32 * wave;
+    const size_t kv_base = ((size_t)b * Hkv + g) * (size_t)Nk + k_row0;
+    store_tile_rows<D>(dk, scale, ksm[wave], dK + kv_base * D, D, Nk - k_row0, lane);
+    store_tile_rows<D>(dv, 1.f, ksm[wave], dV + kv_base * D, D, Nk - k_row0, lane);
+  } else if (jw < Nk) {
     __bf16* dkp = dK + (((size_t)b * Hkv + g) * (size_t)Nk + jw) * D;
     __bf16* dvp = dV + (((size_t)b * Hkv + g) * (size_t)Nk + jw) * D;
 #pragma unroll
@@ -515,19 +525,10 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
 
   // Lane (query qrow, hh) register r of block nb holds column 32 nb + 8 (r/4) + 4 hh + r%4.
-  if (qrow < Nq) {
-    __bf16* dst = dQ + (hq + qrow) * D;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int n = 32 * nb + 8 * r4 + 4 * hh;
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[nb][4 * r4 + 0] * scale, acc[nb][4 * r4 + 1] * scale);
-        w[1] = pack_bf16x2(acc[nb][4 * r4 + 2] * scale, acc[nb][4 * r4 + 3] * scale);
-        *(u32x2*)(dst + n) = w;
-      }
-  }
+  // Stored as whole rows through the wave's quarter of the idle K/V buffers.
+  static_assert(2 * 32 * ROW <= 2 * TILE, "dQ staging fits the K/V buffers");
+  store_tile_rows<D>(acc, scale, (wave < 2 ? sm0 : sm1) + (wave & 1) * 32 * ROW,
+                     dQ + (hq + wave_row_lo) * D, D, Nq - wave_row_lo, lane);
 }
 
 template <int D, bool BAND>

@@ -160,6 +160,42 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Stores a wave's 32 x D tile, held in the C layout of 32x32 MFMAs (lane
+// (row l % 32, half l / 32) register r of block nb = column
+// 32 nb + 8 (r / 4) + 4 (l / 32) + r % 4), times `mul`, in bf16 as whole rows:
+// the tile goes through `stage` (32 * 2D bytes of LDS the wave alone uses,
+// 16-byte chunk c of row r at chunk c ^ (r % chunks-per-row): conflict-free
+// both ways), then each lane stores 16 bytes and every instruction writes
+// whole rows.  Row r goes to dst + r * row_stride; rows >= rows_valid are
+// skipped.  Storing the C layout directly writes 32 rows in 16-byte pieces
+// per instruction, which measured slower.
+template <int D>
+__device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[D / 32], float mul,
+                                                char* stage, __bf16* dst, size_t row_stride,
+                                                int rows_valid, int lane) {
+  constexpr int ROW = 2 * D;
+  constexpr int CPR = ROW / 16;   // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;   // rows per store instruction
+  const int li = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int c = 4 * nb + r4;  // chunk of columns 32 nb + 8 r4 .. + 7
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[nb][4 * r4 + 0] * mul, acc[nb][4 * r4 + 1] * mul);
+      w[1] = pack_bf16x2(acc[nb][4 * r4 + 2] * mul, acc[nb][4 * r4 + 3] * mul);
+      *(u32x2*)(stage + li * ROW + ((c ^ (li & (CPR - 1))) * 16) + hh * 8) = w;
+    }
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR;
+    const int c = lane % CPR;
+    const u32x4 v = *(const u32x4*)(stage + r * ROW + ((c ^ (r & (CPR - 1))) * 16));
+    if (r < rows_valid) *(u32x4*)(dst + (size_t)r * row_stride + c * 8) = v;
+  }
+}
+
 // Wave-uniform "any lane true".
 __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 

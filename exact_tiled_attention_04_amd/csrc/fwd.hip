@@ -567,35 +567,14 @@ void fwd_bf16_kernel(
     }
     return;
   }
-  // Epilogue: one division per row, O in bf16, LSE in natural log.  The
-  // wave's 32 x D tile of O goes through its own slice of the (now idle) K/V
-  // buffers, so the global stores write whole rows: 16-byte chunk c of row r
-  // sits at chunk c ^ (r % chunks-per-row) of the row.
+  // Epilogue: one division per row, O in bf16 stored as whole rows through
+  // the wave's slice of the (now idle) K/V buffers, LSE in natural log.
   {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     static_assert(NW * 32 * ROW <= 4 * TILE, "O staging fits the K/V buffers");
-    char* stage = (wave < 2 ? smem0 + wave * 32 * ROW : smem1 + (wave - 2) * 32 * ROW);
-    constexpr int CPR = ROW / 16;        // 16-byte chunks per row
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int c = 4 * nb + r4;  // 16-byte chunk of columns 32 nb + 8 r4 .. + 7
-        u32x2 w;
-        w[0] = pack_bf16x2(o[nb][4 * r4 + 0] * inv, o[nb][4 * r4 + 1] * inv);
-        w[1] = pack_bf16x2(o[nb][4 * r4 + 2] * inv, o[nb][4 * r4 + 3] * inv);
-        *(u32x2*)(stage + li * ROW + ((c ^ (li & (CPR - 1))) * 16) + hh * 8) = w;
-      }
-    constexpr int RPI2 = 64 / CPR;       // rows per store instruction
-#pragma unroll
-    for (int i = 0; i < 32 / RPI2; ++i) {
-      const int r = i * RPI2 + lane / CPR;
-      const int c = lane % CPR;
-      const u32x4 v = *(const u32x4*)(stage + r * ROW + ((c ^ (r & (CPR - 1))) * 16));
-      const int row = wave_row_lo + r;
-      if (row < Nq)
-        *(u32x4*)(Op + (size_t)row * (PACKED ? (size_t)H * D : (size_t)D) + c * 8) = v;
-    }
+    char* stage = wave < 2 ? smem0 + wave * 32 * ROW : smem1 + (wave - 2) * 32 * ROW;
+    const size_t rs = PACKED ? (size_t)H * D : (size_t)D;
+    store_tile_rows<D>(o, inv, stage, Op + (size_t)wave_row_lo * rs, rs, Nq - wave_row_lo, lane);
     if (qrow < Nq && hh == 0) Lp[qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
   }
 }
