@@ -552,20 +552,15 @@ void fwd_bf16_kernel(
 
   const float l_tot = halves_sum(l_run);
   if (SPLIT) {
-    // Unnormalised partial: o, the base-2 reference max and the sum, merged
-    // by fwd_merge_kernel.
+    // Unnormalised partial: o (as whole rows through the wave's slice of the
+    // idle K/V buffers), the base-2 reference max and the sum, merged by
+    // fwd_merge_kernel.
+    const size_t prow0 = (((size_t)bh * n_qtiles + qt) * n_chunks + chunk) * BR + wave * 32;
+    static_assert(NW * 32 * 256 <= 4 * TILE, "partial staging fits the K/V buffers");
+    store_tile_rows_f32<D>(o, wave < 2 ? smem0 + wave * 32 * 256 : smem1 + (wave - 2) * 32 * 256,
+                           part + prow0 * D, D, Nq - wave_row_lo, lane);
     if (qrow < Nq) {
-      const size_t prow = (((size_t)bh * n_qtiles + qt) * n_chunks + chunk) * BR + wave * 32 + li;
-      float* po = part + prow * D;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          f32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = o[nb][4 * r4 + e];
-          *(f32x4*)(po + 32 * nb + 8 * r4 + 4 * hh) = w;
-        }
+      const size_t prow = prow0 + li;
       if (hh == 0) {
         float* pml = part + (size_t)BH * n_qtiles * n_chunks * BR * D + prow * 2;
         pml[0] = m_run;
