@@ -603,7 +603,7 @@ int attn_plan_describe(int phase, int B, int H, int Hkv, int Nq, int Nk, int d, 
   } else if (phase == ATTN_PHASE_BWD) {
     if (check_bwd_shape(B, H, Hkv, Nq, Nk, d, 1.f, dtype) != ATTN_OK) return -1;
     n = snprintf(tmp, sizeof(tmp),
-                 "phase=bwd kernels=bwd_pre+bwd_dkdv_mfma32x32x16+bwd_dq_mfma32x32x16 d=%d "
+                 "phase=bwd kernels=bwd_dq_mfma32x32x16(+D,LSE2)+bwd_dkdv_mfma32x32x16 d=%d "
                  "causal=%d dkdv: key_tile=128 (4 waves x 32 keys, K in LDS) query_tile=32 grid=%lld "
                  "(B*Hkv*ceil(Nk/128)); dq: query_tile=128 key_tile=32 grid=%lld "
                  "(B*H*ceil(Nq/128)); deterministic (no atomics)",

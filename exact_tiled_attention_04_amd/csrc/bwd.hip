@@ -11,8 +11,6 @@
 //
 // Kernels (no atomics; every output element has exactly one writer, so all
 // three gradients are deterministic):
-//   bwd_pre:  D = rowsum(dO * O) and LSE2 = LSE * log2(e) in fp32 (rows that
-//             see no key get LSE2 = +inf, hence P = 0).
 //   bwd_dkdv: one workgroup per (batch, KV head, 128-key tile), four waves of
 //             32 keys.  V of the wave's keys stays in registers and K in a
 //             wave-private LDS tile (32 registers fewer: two waves per SIMD
@@ -24,8 +22,11 @@
 //             and dS, and accumulates dV^T += dO^T P and dK^T += Q^T dS with
 //             the transposed operands read by ds_read_b64_tr_b16 (the
 //             softmax scale multiplies dK once, at the end).
-//   bwd_dq:   one workgroup per (batch, head, 128-query tile), four waves of
-//             32 queries, laid out like the forward: S^T = K Q^T and
+//   bwd_dq:   runs first.  One workgroup per (batch, head, 128-query tile),
+//             four waves of 32 queries, laid out like the forward.  Each lane
+//             first forms its row's D = rowsum(dO * O) and LSE2 = LSE log2(e)
+//             (rows that see no key get LSE2 = +inf, hence P = 0) and leaves
+//             them in the workspace for bwd_dkdv.  Then S^T = K Q^T and
 //             dP^T = V dO^T with the queries along the lanes, then
 //             dQ^T += K^T dS^T with K^T read transposed from the same LDS
 //             tile (scaled once at the end).  K/V tiles arrive by direct
@@ -63,36 +64,6 @@ __device__ __forceinline__ int snake_order(int w, int n) {
   return w;
 }
 
-
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ O,
-                                                      const __bf16* __restrict__ dO,
-                                                      const float* __restrict__ LSE,
-                                                      float* __restrict__ Dsum,
-                                                      float* __restrict__ LSE2, long long rows) {
-  constexpr int CH = D / 8;
-  constexpr int RPB = 256 / CH;  // rows per block
-  const int t = threadIdx.x;
-  const long long row = (long long)blockIdx.x * RPB + t / CH;
-  const int c = t % CH;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 a = *(const u32x4*)(O + row * D + 8 * c);
-    const u32x4 b = *(const u32x4*)(dO + row * D + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc += bf16_bits_to_float(a[e] & 0xffff) * bf16_bits_to_float(b[e] & 0xffff);
-      acc += bf16_bits_to_float(a[e] >> 16) * bf16_bits_to_float(b[e] >> 16);
-    }
-  }
-#pragma unroll
-  for (int m = CH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && c == 0) {
-    Dsum[row] = acc;
-    const float l = LSE[row];
-    LSE2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
-  }
-}
 
 // ----------------------------------------------------------------- dK, dV
 
@@ -352,7 +323,8 @@ template <int D, bool BAND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                   const float* __restrict__ LSE2, const float* __restrict__ Dsum,
+                   const __bf16* __restrict__ O, const float* __restrict__ LSE,
+                   float* __restrict__ LSE2, float* __restrict__ Dsum,
                    __bf16* __restrict__ dQ, int B, int H, int Hkv, int Nq, int Nk, float scale,
                    float scale_log2, int n_qtiles, int win_left, int win_right) {
   constexpr int NT = 256;
@@ -402,13 +374,35 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const buf_rsrc krs = make_rsrc(K + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
   const buf_rsrc vrs = make_rsrc(V + ((size_t)b * Hkv + g) * (size_t)Nk * D, (unsigned)Nk * ROW);
   bf16x8 qf[KS], of[KS];
+  // D = rowsum(dO * O) and the base-2 LSE of this lane's row are formed here
+  // (the lane and its partner lane ^ 32 hold the two halves of the row) and
+  // written to the workspace for the dK/dV kernel, which runs next.  Rows
+  // that see no key get LSE2 = +inf, hence P = 0.
+  float dd = 0.f;
+  {
+    const buf_rsrc o_rs = make_rsrc(O + hq * D, (unsigned)Nq * ROW);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(qrs, qrow * ROW + (16 * ks + 8 * hh) * 2, 0));
-    of[ks] = __builtin_bit_cast(bf16x8, buf_load16(ors, qrow * ROW + (16 * ks + 8 * hh) * 2, 0));
+    for (int ks = 0; ks < KS; ++ks) {
+      const int vo = qrow * ROW + (16 * ks + 8 * hh) * 2;
+      const u32x4 qv = buf_load16(qrs, vo, 0);
+      const u32x4 gv = buf_load16(ors, vo, 0);
+      const u32x4 ov = buf_load16(o_rs, vo, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8, qv);
+      of[ks] = __builtin_bit_cast(bf16x8, gv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dd += bf16_bits_to_float(gv[e] & 0xffff) * bf16_bits_to_float(ov[e] & 0xffff);
+        dd += bf16_bits_to_float(gv[e] >> 16) * bf16_bits_to_float(ov[e] >> 16);
+      }
+    }
+    dd += __shfl_xor(dd, 32, 64);
   }
-  const float lse2 = qrow < Nq ? LSE2[hq + qrow] : 0.f;
-  const float dd = qrow < Nq ? Dsum[hq + qrow] : 0.f;
+  const float lse_row = qrow < Nq ? LSE[hq + qrow] : 0.f;
+  const float lse2 = lse_row == -INFINITY ? INFINITY : lse_row * kLog2e;
+  if (hh == 0 && qrow < Nq) {
+    Dsum[hq + qrow] = dd;
+    LSE2[hq + qrow] = lse2;
+  }
 
   int goff[NLOAD];
 #pragma unroll
@@ -531,22 +525,24 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      dQ + (hq + wave_row_lo) * D, D, Nq - wave_row_lo, lane);
 }
 
+// dQ first: it forms D and the base-2 LSE of every query row on the way and
+// leaves them in the workspace for dK/dV (the stream orders the two).
 template <int D, bool BAND>
-hipError_t launch_main(const BwdArgs& a, const float* lse2, const float* dsum,
-                       hipStream_t stream) {
+hipError_t launch_main(const BwdArgs& a, float* lse2, float* dsum, hipStream_t stream) {
   const float sl2 = a.scale * kLog2e;
+  const int n_qt = (a.Nq + kBR - 1) / kBR;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BAND>), dim3((unsigned)(n_qt * a.B * a.H)), dim3(256), 0,
+                     stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
+                     (const __bf16*)a.dO, (const __bf16*)a.O, a.LSE, lse2, dsum,
+                     (__bf16*)a.dQ, a.B, a.H, a.Hkv, a.Nq, a.Nk, a.scale, sl2, n_qt, a.win_left,
+                     a.win_right);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int n_kt = (a.Nk + kBK - 1) / kBK;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, BAND>), dim3((unsigned)(n_kt * a.B * a.Hkv)), dim3(256),
                      0, stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
                      (const __bf16*)a.dO, lse2, dsum, (__bf16*)a.dK, (__bf16*)a.dV, a.B, a.H,
                      a.Hkv, a.Nq, a.Nk, a.scale, sl2, a.win_left, a.win_right);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int n_qt = (a.Nq + kBR - 1) / kBR;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, BAND>), dim3((unsigned)(n_qt * a.B * a.H)), dim3(256), 0,
-                     stream, (const __bf16*)a.Q, (const __bf16*)a.K, (const __bf16*)a.V,
-                     (const __bf16*)a.dO, lse2, dsum, (__bf16*)a.dQ, a.B, a.H, a.Hkv, a.Nq, a.Nk,
-                     a.scale, sl2, n_qt, a.win_left, a.win_right);
   return hipGetLastError();
 }
 
@@ -555,11 +551,6 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.B * a.H * a.Nq;
   float* dsum = (float*)a.workspace;
   float* lse2 = dsum + rows;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, (const __bf16*)a.O, (const __bf16*)a.dO, a.LSE, dsum, lse2, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   return a.band ? launch_main<D, true>(a, lse2, dsum, stream)
                 : launch_main<D, false>(a, lse2, dsum, stream);
 }
