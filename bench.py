@@ -358,7 +358,7 @@ def main():
                         "value": round(gemm_flops / (extra["vendor_gemm"][0] * 1e-3) / 1e12, 1),
                         "unit": "TFLOP/s"},
         "launches_and_temporary_bytes": {
-            "fwd": [1, 0], "decode": [2, dws.numel()], "bwd": [3, bws.numel()],
+            "fwd": [1, 0], "decode": [2, dws.numel()], "bwd": [2, bws.numel()],
             "fwd_small_grid": [2, sws_bytes], "varlen": [1, 0], "paged_prefill": [1, 0],
             "block_sparse": [1, 0]},
     }
