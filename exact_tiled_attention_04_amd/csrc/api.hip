@@ -33,7 +33,7 @@ attn_status_t ok() {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-constexpr int kNumCU = 256;        // MI355X compute units
+using eta::kNumCU;
 
 constexpr long long kMaxGrid = 0x7fffffffLL;
 
@@ -104,33 +104,6 @@ bool window_sides(int window_left, int window_right, int* left, int* right) {
 }
 
 // ----------------------------------------------------------------- decode
-
-int plan_decode_chunk(int num_seqs, int Hkv, int max_context, int chunk_tokens) {
-  if (chunk_tokens > 0) return chunk_tokens;
-  // About 64 split waves per CU if every sequence were max_context long
-  // (about half that for contexts spread uniformly below it): enough
-  // independent K/V streams to keep HBM busy, each long enough to amortise
-  // its start-up, with partials a small fraction of the cache bytes.
-  // Chunks are multiples of 32 tokens (measured best: 1024 tokens for 64
-  // sequences x 8 KV heads x 32k context).
-  const long long target_units = 64LL * kNumCU;
-  const long long pairs = (long long)num_seqs * Hkv;
-  long long chunk = (pairs * (long long)max_context + target_units - 1) / target_units;
-  chunk = (chunk + 31) / 32 * 32;
-  // Chunks of at least 1024 tokens unless that leaves fewer than 2048
-  // chunk-waves at max_context (eight per CU, the split waves resident at
-  // once): shorter chunks write more partials than they gain in balance
-  // (32 sequences of 8192 tokens: 128-token chunks 4.63 TB/s, 1024-token
-  // chunks 5.77; 16 x 32k-64k, 64 x 8k-16k: +2-3%; the other swept batches
-  // within 1%).
-  long long lo = pairs * (long long)max_context / 2048;
-  if (lo > 1024) lo = 1024;
-  lo = lo / 32 * 32;
-  if (chunk < lo) chunk = lo;
-  if (chunk < 64) chunk = 64;
-  if (chunk > 4064) chunk = 4064;
-  return (int)chunk;
-}
 
 attn_status_t check_decode_shape(int num_seqs, int Hq, int Hkv, int d, int block_size,
                                  int num_blocks, int max_blocks_per_seq, int max_context,
@@ -484,16 +457,27 @@ attn_status_t attn_fwd_splitkv(const void* Q, const void* K, const void* V, void
                   workspace);
 }
 
+// Workspace of a decode with Hkv = Hq / G KV heads.
+size_t decode_ws_for(int num_seqs, int Hq, int G, int d, int max_context, int chunk_tokens) {
+  const long long pairs = (long long)num_seqs * (Hq / G);
+  const long long waves = eta::decode_split_waves(pairs, d, max_context, chunk_tokens / 32);
+  return eta::decode_workspace_bytes(pairs, G, d, waves);
+}
+
 size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_context,
                                         int chunk_tokens) {
   if (num_seqs < 1 || Hq < 1 || (d != 64 && d != 128) || max_context < 0 || chunk_tokens < 0 ||
       chunk_tokens % 32 != 0 || chunk_tokens > 4064)
     return 0;
-  // The plan only needs Hkv to pick a chunk; the workspace must cover the
-  // largest chunk count any Hkv could lead to, i.e. the smallest chunk.
-  const int chunk = chunk_tokens > 0 ? chunk_tokens : plan_decode_chunk(num_seqs, 1, max_context, 0);
-  const int n_chunks = (max_context + chunk - 1) / chunk;
-  return eta::decode_workspace_bytes(num_seqs, Hq, d, n_chunks > 0 ? n_chunks : 1);
+  // The size depends on the group size G = Hq / Hkv, which the caller has
+  // not given: cover every G the decode accepts.
+  size_t most = 0;
+  for (int G = 1; G <= 16 && G <= Hq; ++G)
+    if (Hq % G == 0) {
+      const size_t b = decode_ws_for(num_seqs, Hq, G, d, max_context, chunk_tokens);
+      if (b > most) most = b;
+    }
+  return most;
 }
 
 attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache,
@@ -530,9 +514,13 @@ attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* 
   if (block_stride >= (1LL << 30))
     return fail(ATTN_ERR_UNSUPPORTED, "block_stride=%lld elements exceeds 2^30",
                 (long long)block_stride);
-  const int chunk = plan_decode_chunk(num_seqs, Hkv, max_context, chunk_tokens);
-  const int n_chunks = (max_context + chunk - 1) / chunk;
-  const size_t need = eta::decode_workspace_bytes(num_seqs, Hq, d, n_chunks > 0 ? n_chunks : 1);
+  const long long pairs = (long long)num_seqs * Hkv;
+  const long long n_waves = eta::decode_split_waves(pairs, d, max_context, chunk_tokens / 32);
+  // Segment ids (split wave + pair index) and the split grid stay in int.
+  if (n_waves + pairs > kMaxGrid)
+    return fail(ATTN_ERR_UNSUPPORTED, "decode needs %lld split waves for %lld pairs",
+                n_waves, pairs);
+  const size_t need = eta::decode_workspace_bytes(pairs, Hq / Hkv, d, n_waves);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -542,7 +530,7 @@ attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* 
                     d,        block_size,  num_blocks,   max_blocks_per_seq,
                     max_context, block_stride, token_stride, head_stride, scale,
                     workspace};
-  eta::DecodePlan p{chunk, n_chunks};
+  eta::DecodePlan p{chunk_tokens / 32, eta::decode_target_waves(d), n_waves};
   hipError_t e = eta::launch_decode(a, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -593,13 +581,13 @@ int attn_plan_describe(int phase, int B, int H, int Hkv, int Nq, int Nk, int d, 
     if (check_decode_shape(B, H, Hkv, d, 16, 1, (Nk + 15) / 16 > 0 ? (Nk + 15) / 16 : 1, Nk, 0) !=
         ATTN_OK)
       return -1;
-    const int chunk = plan_decode_chunk(B, Hkv, Nk, 0);
-    const int n_chunks = (Nk + chunk - 1) / chunk;
+    const long long waves = eta::decode_split_waves((long long)B * Hkv, d, Nk, 0);
     n = snprintf(tmp, sizeof(tmp),
                  "phase=decode kernel=decode_split_mfma16x16x32+decode_merge d=%d G=%d "
-                 "chunk_tokens=%d max_chunks=%d split_waves<=%lld (seqs*Hkv*chunks) "
-                 "merge_workgroups=%lld",
-                 d, H / Hkv, chunk, n_chunks, (long long)B * Hkv * n_chunks, (long long)B * H);
+                 "split=balanced (equal 32-token step ranges of all seq x KV-head pairs, "
+                 ">= %d steps per wave, %d waves) split_waves<=%lld merge_workgroups=%lld",
+                 d, H / Hkv, eta::kDecodeMinSteps, eta::decode_target_waves(d), waves,
+                 (long long)B * H);
   } else if (phase == ATTN_PHASE_BWD) {
     if (check_bwd_shape(B, H, Hkv, Nq, Nk, d, 1.f, dtype) != ATTN_OK) return -1;
     n = snprintf(tmp, sizeof(tmp),

@@ -11,22 +11,29 @@
 // the online-softmax rescaling) and its grouped-query paragraph (the query
 // heads sharing one KV head read it once).
 //
-// Split kernel: one wave per (sequence, KV head, context chunk).  The G query
-// heads of the group are the columns of a 16x16x32 MFMA (G <= 16), so every
-// K and V byte is read from HBM once and used by all G heads.  Per 32 tokens
-// (two 16-token groups): K rows go straight from HBM into MFMA A-operand
-// registers (S^T = K Q^T); V rows are staged in a wave-private LDS tile and
-// read transposed (ds_read_b64_tr_b16) as the A operand of o^T += V^T P^T.
-// Block sizes that are multiples of 16 take a path with wave-uniform page
-// addressing through buffer resources; other block sizes look each token's
-// page up per lane.
-// The next 32 tokens are fetched while the current ones are computed.
+// Split kernel: the contexts of all (sequence, KV head) pairs, in 32-token
+// steps laid end to end, are cut into equal ranges, one per wave (the plan in
+// kernels.hpp), so every wave streams the same number of cache bytes and a
+// wave whose range crosses a pair boundary writes one partial per pair it
+// touches.  Within a pair, the G query heads of the group are the columns
+// of a 16x16x32 MFMA (G <= 16), so every K and V byte is read from HBM once
+// and used by all G heads.  Per 32 tokens
+// (two 16-token groups): K and V arrive as whole rows, several per load.  On
+// the path for block sizes that are multiples of 16 (wave-uniform page
+// addressing through buffer resources), K rows are staged in a wave-private
+// LDS tile and read back as the MFMA A operand of S^T = K Q^T; on the path
+// for other block sizes (each token's page looked up per lane) they go from
+// HBM straight into A-operand registers.  V rows are staged in a second LDS
+// tile and read transposed (ds_read_b64_tr_b16) as the A operand of
+// o^T += V^T P^T.
+// The next 32 tokens are fetched while the current ones are computed.  Cache
+// rows are loaded non-temporal: each is read once per launch.
 // Tokens past the context (poisoned or stale page slots) never reach the
 // result: their scores are replaced by -inf and their V rows by zeros.
 //
 // Merge kernel: one workgroup per (query head, sequence), one thread per
-// output column: M = max_c m_c, w_c = 2^(m_c - M), l = sum w_c l_c,
-// O = sum w_c o_c / l, LSE = (M + log2 l) ln 2.
+// output column, over the pair's partials c: M = max_c m_c, w_c = 2^(m_c - M),
+// l = sum w_c l_c, O = sum w_c o_c / l, LSE = (M + log2 l) ln 2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -34,13 +41,35 @@ namespace eta {
 
 namespace {
 
-constexpr int kTok = 32;  // tokens per inner step (two 16-token pages)
-// Longest context chunk one split wave handles (its block-table entries are
-// held in four registers: 256 pages of >= 16 tokens).
-constexpr int kMaxChunk = 4064;
+constexpr int kTok = kDecodeStepTokens;  // tokens per inner step (two 16-token groups)
 
-// Two waves per SIMD (eight per CU), each with the next 32 tokens' K and V
-// in flight: enough bytes outstanding to cover HBM latency without spills.
+// Swizzle of the decode K tile: chunk c of row r sits at c ^ (r mod chunks per
+// row).  The tile is written as whole rows (conflict-free for any swizzle)
+// and read in the 16x16x32 A layout (lane: row l % 16, chunk 4 ks + l / 16),
+// for which this swizzle measured conflict-free on gfx950 and tile_swz or
+// decode_swz measured two-way conflicts.
+template <int D>
+__device__ __forceinline__ int decode_k_swz(int row) {
+  return row & (D / 8 - 1);
+}
+// The paged kernel walks a segment in pieces of at most kDecodeMaxSteps
+// steps (4064 tokens): a piece's block-table entries fit four registers of
+// 64 lanes (at most 254 pages of >= 16 tokens, as pieces start on a step
+// boundary).
+static_assert(kDecodeMaxSteps * kTok <= 4064, "piece block-table entries exceed 256");
+
+// Steps of K and of V in flight ahead of the one being computed (K 3, 4 or
+// 5 and V 2 or 3 steps ahead at one wave per SIMD measured the same as 2 and
+// 1 with the automatic split).
+#ifndef ETA_DECODE_K_AHEAD
+#define ETA_DECODE_K_AHEAD 2
+#endif
+#ifndef ETA_DECODE_V_AHEAD
+#define ETA_DECODE_V_AHEAD 1
+#endif
+
+// Registers for two waves per SIMD: the automatic split runs one per SIMD,
+// a caller-fixed range length can ask for more waves than that.
 #ifndef ETA_DECODE_WAVES_PER_EU
 #define ETA_DECODE_WAVES_PER_EU 2
 #endif
@@ -56,50 +85,112 @@ constexpr int kMaxChunk = 4064;
 #define ETA_DECODE_WG_WAVES 4
 #endif
 
-// Work order of the split kernels.  Work items enumerate the live chunks
-// only: first every sequence's full chunks (sequence by sequence), then the
-// shorter last chunks of the sequences whose context is not a multiple of
-// chunk_tokens, so the short items fill the end of the launch (longest work
-// first).  A wave's slot id = item * Hkv + g.  The grid is sized for the
-// largest possible count, so the live work is dispatched first and the
-// surplus slots at the end exit at once (measured faster than a grid with
-// dead slots interleaved through it).  The wave finds its sequence by an
-// inclusive scan of the per-sequence counts of 64 sequences at a time.
-// Returns g and sets s = -1 for a surplus slot.
-__device__ __forceinline__ int live_item(int slot, int Hkv, const int* __restrict__ ctx_lens,
-                                         int num_seqs, int max_context, int chunk_tokens,
-                                         int lane, int& s_out, int& chunk_out) {
-  int item = slot / Hkv;
-  const int g = slot % Hkv;
-  int s = -1, chunk = 0;
-  for (int pass = 0; pass < 2 && s < 0; ++pass) {
-    for (int base = 0; base < num_seqs; base += 64) {
-      const int sq = base + lane;
-      int nc = 0, full = 0;
-      if (sq < num_seqs) {
-        const int c = min(ctx_lens[sq], max_context);
-        full = c > 0 ? c / chunk_tokens : 0;
-        nc = pass == 0 ? full : (c > 0 && c % chunk_tokens != 0 ? 1 : 0);
-      }
-      int incl = nc;
+// Steps of a context of ctx tokens.
+__device__ __forceinline__ int ctx_steps(int ctx) { return ctx > 0 ? (ctx + kTok - 1) / kTok : 0; }
+
+__device__ __forceinline__ long long uniform64(long long v) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+// Where a split wave's work starts.  Pair (s, g) owns steps
+// [seq_base(s) + g n_s, seq_base(s) + (g + 1) n_s), n_s = ceil(ctx_s / 32);
+// wave w takes steps [w q, min((w + 1) q, U)).  The wave reads the
+// sequences' contexts 64 at a time (one per lane): a reduction gives U, and
+// with it q when the caller left it open; an inclusive scan finds the
+// sequence that holds step w q.
+struct SplitPos {
+  long long a, b;      // the wave's steps [a, b)
+  long long seq_base;  // first step of sequence s
+  int s, n, ctx, g;    // sequence, its steps, its context, KV head
+};
+
+// False when the wave has no steps.
+__device__ __forceinline__ bool split_start(int w, const int* __restrict__ ctx_lens, int num_seqs,
+                                            int Hkv, int max_context, int steps_fixed,
+                                            int target_waves, int lane, SplitPos& sp) {
+  auto ctx_of = [&](int sq) -> int {
+    return sq < num_seqs ? max(0, min(ctx_lens[sq], max_context)) : 0;
+  };
+  long long U = 0;
+  for (int base = 0; base < num_seqs; base += 64) {
+    long long c = (long long)ctx_steps(ctx_of(base + lane)) * Hkv;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += t;
-      }
-      const unsigned long long hit = __ballot(incl > item);
-      if (hit) {
-        const int l = __builtin_ctzll(hit);
-        s = base + l;
-        chunk = pass == 0 ? item - (__shfl(incl, l, 64) - __shfl(nc, l, 64)) : __shfl(full, l, 64);
-        break;
-      }
-      item -= __shfl(incl, 63, 64);
-    }
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+    U += c;
   }
-  s_out = __builtin_amdgcn_readfirstlane(s);
-  chunk_out = __builtin_amdgcn_readfirstlane(chunk);
-  return g;
+  U = uniform64(U);
+  long long q = steps_fixed;
+  if (q <= 0) {
+    q = (U + target_waves - 1) / target_waves;
+    if (q < kDecodeMinSteps) q = kDecodeMinSteps;
+  }
+  const long long a = (long long)w * q;
+  if (a >= U) return false;
+  sp.a = a;
+  sp.b = a + q < U ? a + q : U;
+  long long run = 0;
+  for (int base = 0; base < num_seqs; base += 64) {
+    const int ctx = ctx_of(base + lane);
+    const int n = ctx_steps(ctx);
+    const long long c = (long long)n * Hkv;
+    long long incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    const unsigned long long hit = __ballot(run + incl > a);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      sp.s = base + l;
+      sp.n = __builtin_amdgcn_readfirstlane(__shfl(n, l, 64));
+      sp.ctx = __builtin_amdgcn_readfirstlane(__shfl(ctx, l, 64));
+      sp.seq_base = uniform64(run + __shfl(incl - c, l, 64));
+      sp.g = (int)((a - sp.seq_base) / sp.n);
+      return true;
+    }
+    run += __shfl(incl, 63, 64);
+  }
+  return false;  // not reached: a < U
+}
+
+// One segment of a wave's range: the steps it holds of pair (s, g), as
+// tokens [t_begin, t_end) of that pair's context.  After the segment the
+// wave moves to the next pair with steps (KV head minor).  Returns false at
+// the end of the range.
+struct SplitSeg {
+  int t_begin, t_end;
+  bool first, last;  // the segment holds the pair's first / last step
+};
+__device__ __forceinline__ SplitSeg split_segment(const SplitPos& sp) {
+  const long long P = sp.seq_base + (long long)sp.g * sp.n;
+  const int l0 = (int)(sp.a - P);
+  const int l1 = sp.b - P < sp.n ? (int)(sp.b - P) : sp.n;
+  SplitSeg sg;
+  sg.t_begin = l0 * kTok;
+  sg.t_end = min(sp.ctx, l1 * kTok);
+  sg.first = l0 == 0;
+  sg.last = l1 == sp.n;
+  return sg;
+}
+__device__ __forceinline__ bool split_next(SplitPos& sp, const int* __restrict__ ctx_lens,
+                                           int num_seqs, int Hkv, int max_context) {
+  const long long P = sp.seq_base + (long long)sp.g * sp.n;
+  sp.a = sp.b - P < sp.n ? sp.b : P + sp.n;
+  if (sp.a >= sp.b) return false;
+  if (++sp.g < Hkv) return true;
+  sp.g = 0;
+  sp.seq_base += (long long)sp.n * Hkv;
+  do {
+    if (++sp.s >= num_seqs) return false;  // not reached: steps remain
+    sp.ctx = max(0, min(ctx_lens[sp.s], max_context));
+    sp.n = ctx_steps(sp.ctx);
+  } while (sp.n == 0);
+  sp.ctx = __builtin_amdgcn_readfirstlane(sp.ctx);
+  sp.n = __builtin_amdgcn_readfirstlane(sp.n);
+  return true;
 }
 
 template <int D>
@@ -108,10 +199,11 @@ __attribute__((amdgpu_waves_per_eu(ETA_DECODE_WAVES_PER_EU)))
 void decode_split_paged_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc, const __bf16* __restrict__ Vc,
     const int* __restrict__ block_table, const int* __restrict__ ctx_lens,
-    float* __restrict__ part_o, float* __restrict__ part_ml, int num_seqs, int Hq, int Hkv,
-    int G, int block_size, int num_blocks, int max_blocks, int max_context, int chunk_tokens,
-    int n_chunks_max, long long block_stride, long long token_stride, long long head_stride,
-    float scale_log2, unsigned page_magic, int page_shift) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, int* __restrict__ seg_first,
+    int* __restrict__ seg_last, int num_seqs, int Hq, int Hkv, int G, int block_size,
+    int num_blocks, int max_blocks, int max_context, int steps_fixed, int target_waves,
+    long long block_stride, long long token_stride, long long head_stride, float scale_log2,
+    unsigned page_magic, int page_shift) {
   constexpr int KS = D / 32;          // k-steps of S^T = K Q^T (32 d each)
   constexpr int NB = D / 16;          // 16-row blocks of o^T
   constexpr int CH = D / 8;           // 16-byte chunks per row
@@ -119,51 +211,37 @@ void decode_split_paged_kernel(
   constexpr int TPI = 64 / CH;        // tokens per V load instruction
 
   __shared__ __attribute__((aligned(16))) __bf16 vs_all[ETA_DECODE_WG_WAVES][kTok * D];
+  // K goes through a wave-private LDS tile too: global loads take whole
+  // token rows (4 rows x 256 bytes per instruction at d = 128) and the MFMA
+  // operand is read back from LDS; loading the operand layout directly
+  // (16 rows x 64 bytes per instruction) reached less of the HBM rate.
+  __shared__ __attribute__((aligned(16))) __bf16 ks_all[ETA_DECODE_WG_WAVES][kTok * D];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int s, chunk;
-  const int g = live_item(blockIdx.x * ETA_DECODE_WG_WAVES + wave, Hkv, ctx_lens, num_seqs,
-                          max_context, chunk_tokens, lane, s, chunk);
-  if (s < 0) return;
-  const int ctx = min(ctx_lens[s], max_context);
-  const int t_begin = chunk * chunk_tokens;
-  if (t_begin >= ctx) return;
-  const int t_end = min(ctx, t_begin + chunk_tokens);
+  const int w = blockIdx.x * ETA_DECODE_WG_WAVES + wave;
+  SplitPos sp;
+  if (!split_start(w, ctx_lens, num_seqs, Hkv, max_context, steps_fixed, target_waves, lane, sp))
+    return;
+  int t_begin = 0, t_end = 0;  // the current piece's tokens of pair (sp.s, sp.g)
 
   __bf16* vs = vs_all[wave];
+  __bf16* kst = ks_all[wave];
   const int qc = lane & 15;   // query column (head within the group) / A row
   const int g4 = lane >> 4;   // 16-lane group
 
   bf16x8 qf[KS];
-  {
-    const bool ok = qc < G;
-    const __bf16* src = Q + ((size_t)s * Hq + (size_t)g * G + (ok ? qc : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = ok ? *(const u32x4*)(src + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  const int* bt = block_table + (size_t)s * max_blocks;
   const int ts2 = (int)(token_stride * 2);  // bytes between tokens
-  // Per-lane byte offsets inside a 16-token group: the K row of token qc
-  // (A operand, d = 32 ks + 8 g4 + e) and this lane's V chunk.
-  const int koff = qc * ts2 + 16 * g4;
+  // This lane's 16-byte chunk of a K or V row inside a 16-token group (the
+  // wave loads TPI whole rows per instruction).
   const int voff = (lane / CH) * ts2 + (lane % CH) * 16;
 
-  // The chunk's block-table entries (up to 4 * 64 logical pages, enough for
-  // kMaxChunk tokens), one per lane of bt_r[i], loaded once: page lookups
-  // are register reads (v_readlane), so no step waits on memory before it
-  // can issue its K/V loads.
-  const int bt_base = t_begin / block_size;
+  // The current piece's block-table entries (up to 4 * 64 logical pages,
+  // enough for kDecodeMaxSteps steps), one per lane of bt_r[i], loaded at its
+  // start: page lookups are register reads (v_readlane), so no step waits on
+  // memory before it can issue its K/V loads.
+  int bt_base = 0;
   int bt_r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lp = bt_base + 64 * i + lane;
-    bt_r[i] = lp < max_blocks ? bt[lp] : -1;
-  }
   auto page_of = [&](int logical) -> int {
     const int idx = logical - bt_base;  // 0 <= idx < 256 by the chunk limit
     const int r = idx >> 6, l = idx & 63;
@@ -188,7 +266,7 @@ void decode_split_paged_kernel(
       if (ph < 0 || ph >= num_blocks) live = 0;
       else
         base = (long long)ph * block_stride + (long long)slot0 * token_stride +
-               (long long)g * head_stride;
+               (long long)sp.g * head_stride;
     }
     live = __builtin_amdgcn_readfirstlane(live);
     const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)base);
@@ -201,33 +279,35 @@ void decode_split_paged_kernel(
     return r;
   };
 
-  u32x4 ka[2][KS], kb[2][KS], kc[2][KS], vr[VL];
-  int la[2], lb[2], lc[2];
-  auto load_k = [&](int t0, u32x4 (&kd)[2][KS], int (&live)[2]) {
+  // Register rings: K of the next NKB - 1 steps and V of the next NVB steps
+  // are in flight while a step is computed.
+  constexpr int NKB = ETA_DECODE_K_AHEAD + 1;
+  constexpr int NVB = ETA_DECODE_V_AHEAD;
+  u32x4 kbuf[NKB][VL], vbuf[NVB][VL];
+  int lbuf[NKB][2];
+  auto load_k = [&](int t0, u32x4 (&kd)[VL], int (&live)[2]) {
     const Group g0 = group(t0), g1 = group(t0 + 16);
     live[0] = g0.live;
     live[1] = g1.live;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kd[0][ks] = buf_load16(g0.k, koff + 64 * ks, 0);
-      kd[1][ks] = buf_load16(g1.k, koff + 64 * ks, 0);
+    for (int it = 0; it < VL; ++it) {
+      const int pp = (TPI * it) / 16;
+      kd[it] = buf_load16_nt(pp == 0 ? g0.k : g1.k, voff, (TPI * it - 16 * pp) * ts2);
     }
   };
-  auto load_v = [&](int t0) {
+  auto load_v = [&](int t0, u32x4 (&vr)[VL]) {
     const Group g0 = group(t0), g1 = group(t0 + 16);
 #pragma unroll
     for (int it = 0; it < VL; ++it) {
       const int pp = (TPI * it) / 16;
-      vr[it] = buf_load16(pp == 0 ? g0.v : g1.v, voff, (TPI * it - 16 * pp) * ts2);
+      vr[it] = buf_load16_nt(pp == 0 ? g0.v : g1.v, voff, (TPI * it - 16 * pp) * ts2);
     }
   };
 
   f32x4 o[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run, l_run;
 
-  auto stage_v = [&]() {
+  auto stage_v = [&](const u32x4 (&vr)[VL]) {
 #pragma unroll
     for (int it = 0; it < VL; ++it) {
       const int cid = lane + 64 * it;
@@ -236,14 +316,24 @@ void decode_split_paged_kernel(
       *(u32x4*)(vs + tk * D + ((c ^ decode_swz<D>(tk)) * 8)) = vr[it];
     }
   };
-  auto compute_step = [&](u32x4 (&kd)[2][KS], int (&live)[2]) {
+  auto compute_step = [&](u32x4 (&kd)[VL], int (&live)[2]) {
+#pragma unroll
+    for (int it = 0; it < VL; ++it) {
+      const int cid = lane + 64 * it;
+      const int tk = cid / CH;
+      const int c = cid % CH;
+      *(u32x4*)(kst + tk * D + ((c ^ decode_k_swz<D>(tk)) * 8)) = kd[it];
+    }
     f32x4 sc[2];
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       sc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int tk = 16 * pp + qc;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        sc[pp] = mfma16(__builtin_bit_cast(bf16x8, kd[pp][ks]), qf[ks], sc[pp]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *(const bf16x8*)(kst + tk * D + (((4 * ks + g4) ^ decode_k_swz<D>(tk)) * 8));
+        sc[pp] = mfma16(a, qf[ks], sc[pp]);
+      }
     }
     // Lane (qc, g4) register r of sc[pp] is token 16 pp + 4 g4 + r of the step.
 #pragma unroll
@@ -297,43 +387,92 @@ void decode_split_paged_kernel(
     __asm__ volatile("" ::: "memory");
   };
 
-  // Software pipeline over 32-token steps: K is fetched two steps ahead
-  // through a ring of three register sets, V one step ahead (its registers
-  // are free once the current step is staged in LDS), so about 24 KiB per
-  // wave stay in flight while a step is computed.
-  auto iter = [&](int t0, u32x4 (&kcur)[2][KS], int (&lcur)[2], u32x4 (&kfar)[2][KS],
-                  int (&lfar)[2]) -> bool {
-    stage_v();
-    if (t0 + kTok < t_end) load_v(t0 + kTok);
-    if (t0 + 2 * kTok < t_end) load_k(t0 + 2 * kTok, kfar, lfar);
-    compute_step(kcur, lcur);
+  // Software pipeline over 32-token steps: step u computes from K ring slot
+  // u % NKB after refilling slot (u - 1) % NKB with the K of step u + NKB - 1,
+  // and stages V slot u % NVB in LDS before refilling it with the V of step
+  // u + NVB (a V slot is free once staged).
+  auto iter = [&](int u, int t0) -> bool {
+    stage_v(vbuf[u % NVB]);
+    if (t0 + NVB * kTok < t_end) load_v(t0 + NVB * kTok, vbuf[u % NVB]);
+    if (t0 + (NKB - 1) * kTok < t_end)
+      load_k(t0 + (NKB - 1) * kTok, kbuf[(u + NKB - 1) % NKB], lbuf[(u + NKB - 1) % NKB]);
+    compute_step(kbuf[u % NKB], lbuf[u % NKB]);
     return t0 + kTok < t_end;
   };
-  int t0 = t_begin;
-  load_k(t0, ka, la);
-  load_v(t0);
-  if (t0 + kTok < t_end) load_k(t0 + kTok, kb, lb);
-  while (true) {
-    if (!iter(t0, ka, la, kc, lc)) break;
-    t0 += kTok;
-    if (!iter(t0, kb, lb, ka, la)) break;
-    t0 += kTok;
-    if (!iter(t0, kc, lc, kb, lb)) break;
-    t0 += kTok;
-  }
-
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot = halves_sum(l_tot);
-  if (qc < G) {
-    const size_t row = ((size_t)chunk * num_seqs + s) * Hq + (size_t)g * G + qc;
-    float* dst = part_o + row * D;
+  do {
+    const SplitSeg seg = split_segment(sp);
+    {
+      const bool ok = qc < G;
+      const __bf16* src = Q + ((size_t)sp.s * Hq + (size_t)sp.g * G + (ok ? qc : 0)) * D;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) *(f32x4*)(dst + 16 * nb + 4 * g4) = o[nb];
-    if (g4 == 0) {
-      part_ml[row * 2 + 0] = m_run;
-      part_ml[row * 2 + 1] = l_tot;
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = ok ? *(const u32x4*)(src + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
+        qf[ks] = __builtin_bit_cast(bf16x8, v);
+      }
     }
-  }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+
+    // The segment in pieces of at most kDecodeMaxSteps steps, each with its
+    // block-table entries in registers (the running o, m, l carry over).
+    for (int piece = seg.t_begin; piece < seg.t_end; piece += kDecodeMaxSteps * kTok) {
+      t_begin = piece;
+      t_end = min(seg.t_end, piece + kDecodeMaxSteps * kTok);
+      {
+        const int* bt = block_table + (size_t)sp.s * max_blocks;
+        bt_base = t_begin / block_size;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int lp = bt_base + 64 * i + lane;
+          bt_r[i] = lp < max_blocks ? bt[lp] : -1;
+        }
+      }
+      load_k(t_begin, kbuf[0], lbuf[0]);
+#pragma unroll
+      for (int u = 0; u < NVB; ++u)
+        if (u == 0 || t_begin + u * kTok < t_end) load_v(t_begin + u * kTok, vbuf[u]);
+#pragma unroll
+      for (int u = 1; u + 1 < NKB; ++u)
+        if (t_begin + u * kTok < t_end) load_k(t_begin + u * kTok, kbuf[u], lbuf[u]);
+      // Steps in groups of lcm(NKB, NVB), so every ring slot index is a
+      // compile-time constant.
+      constexpr int kUnroll = NKB % NVB == 0 ? NKB : NKB * NVB;
+      for (int t0 = t_begin;;) {
+        bool more = true;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          if (more) {
+            more = iter(u, t0);
+            t0 += kTok;
+          }
+        }
+        if (!more) break;
+      }
+    }
+
+    // Partial of segment id w + pair: unique, and consecutive over a pair's
+    // segments (both w and the pair index only grow along the steps).
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot = halves_sum(l_tot);
+    const int pair = sp.s * Hkv + sp.g;
+    const int id = w + pair;
+    if (qc < G) {
+      const size_t row = (size_t)id * G + qc;
+      float* dst = part_o + row * D;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) *(f32x4*)(dst + 16 * nb + 4 * g4) = o[nb];
+      if (g4 == 0) {
+        part_ml[row * 2 + 0] = m_run;
+        part_ml[row * 2 + 1] = l_tot;
+      }
+    }
+    if (lane == 0) {
+      if (seg.first) seg_first[pair] = id;
+      if (seg.last) seg_last[pair] = id;
+    }
+  } while (split_next(sp, ctx_lens, num_seqs, Hkv, max_context));
 }
 
 // Generic block sizes: every token's page is looked up on its own lane.
@@ -342,9 +481,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETA_DECODE_
 void decode_split_generic_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ Kc, const __bf16* __restrict__ Vc,
     const int* __restrict__ block_table, const int* __restrict__ ctx_lens,
-    float* __restrict__ part_o, float* __restrict__ part_ml, int num_seqs, int Hq, int Hkv,
-    int G, int block_size, int num_blocks, int max_blocks, int max_context, int chunk_tokens,
-    int n_chunks_max,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int* __restrict__ seg_first,
+    int* __restrict__ seg_last, int num_seqs, int Hq, int Hkv, int G, int block_size,
+    int num_blocks, int max_blocks, int max_context, int steps_fixed, int target_waves,
     long long block_stride, long long token_stride, long long head_stride, float scale_log2) {
   constexpr int KS = D / 32;   // k-steps of S^T = K Q^T (32 d each)
   constexpr int NB = D / 16;   // 16-row blocks of o^T
@@ -355,14 +494,11 @@ void decode_split_generic_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int s, chunk;
-  const int g = live_item(blockIdx.x * 4 + wave, Hkv, ctx_lens, num_seqs, max_context,
-                          chunk_tokens, lane, s, chunk);
-  if (s < 0) return;
-  const int ctx = min(ctx_lens[s], max_context);
-  const int t_begin = chunk * chunk_tokens;
-  if (t_begin >= ctx) return;
-  const int t_end = min(ctx, t_begin + chunk_tokens);
+  const int w = blockIdx.x * 4 + wave;
+  SplitPos sp;
+  if (!split_start(w, ctx_lens, num_seqs, Hkv, max_context, steps_fixed, target_waves, lane, sp))
+    return;
+  int t_begin = 0, t_end = 0;  // the current segment's tokens of pair (sp.s, sp.g)
 
   __bf16* vs = vs_all[wave];
   const int qc = lane & 15;   // query column (head within the group) / A row
@@ -370,19 +506,9 @@ void decode_split_generic_kernel(
 
   // Q^T as the B operand: lane (qc, g4) holds Q[qc][32 ks + 8 g4 + e].
   bf16x8 qf[KS];
-  {
-    const bool ok = qc < G;
-    const __bf16* src = Q + ((size_t)s * Hq + (size_t)g * G + (ok ? qc : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = ok ? *(const u32x4*)(src + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  const int* bt = block_table + (size_t)s * max_blocks;
-  const __bf16* Kg = Kc + (size_t)g * head_stride;
-  const __bf16* Vg = Vc + (size_t)g * head_stride;
+  const int* bt = block_table;
+  const __bf16* Kg = Kc;
+  const __bf16* Vg = Vc;
 
   // Address of token `pos` of this sequence, or null when pos is past the
   // chunk or its block-table entry lies outside the cache.
@@ -404,7 +530,8 @@ void decode_split_generic_kernel(
       live[pp] = __ballot(p != nullptr);
       if (p) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kd[pp][ks] = *(const u32x4*)(p + 32 * ks + 8 * g4);
+        for (int ks = 0; ks < KS; ++ks)
+          kd[pp][ks] = __builtin_nontemporal_load((const u32x4*)(p + 32 * ks + 8 * g4));
       } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kd[pp][ks] = u32x4{0, 0, 0, 0};
@@ -418,14 +545,12 @@ void decode_split_generic_kernel(
       const int tk = cid / CH;
       const int c = cid % CH;
       const __bf16* p = tok_ptr(Vg, t0 + tk);
-      vr[it] = p ? *(const u32x4*)(p + 8 * c) : u32x4{0, 0, 0, 0};
+      vr[it] = p ? __builtin_nontemporal_load((const u32x4*)(p + 8 * c)) : u32x4{0, 0, 0, 0};
     }
   };
 
   f32x4 o[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run, l_run;
 
   // V rows of the current step into the wave's LDS tile (row-major,
   // 16-byte chunks XOR-swizzled by row); frees vr for the next step's loads.
@@ -501,122 +626,166 @@ void decode_split_generic_kernel(
 
   // Software pipeline: V of the current step is staged in LDS before the
   // next step's K and V loads are issued, so they fly during the compute.
-  int t0 = t_begin;
-  load_k(t0, kr, live_r);
-  load_v(t0);
-  while (true) {
-    stage_v();
-    int t1 = t0 + kTok;
-    if (t1 < t_end) {
-      load_v(t1);
-      load_k(t1, kn, live_n);
-    }
-    compute_step(kr, live_r);
-    if (t1 >= t_end) break;
-    t0 = t1;
-    stage_v();
-    t1 = t0 + kTok;
-    if (t1 < t_end) {
-      load_v(t1);
-      load_k(t1, kr, live_r);
-    }
-    compute_step(kn, live_n);
-    if (t1 >= t_end) break;
-    t0 = t1;
-  }
-
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (qc < G) {
-    const size_t row = ((size_t)chunk * num_seqs + s) * Hq + (size_t)g * G + qc;
-    float* dst = part_o + row * D;
+  do {
+    const SplitSeg seg = split_segment(sp);
+    t_begin = seg.t_begin;
+    t_end = seg.t_end;
+    {
+      const bool ok = qc < G;
+      const __bf16* src = Q + ((size_t)sp.s * Hq + (size_t)sp.g * G + (ok ? qc : 0)) * D;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) *(f32x4*)(dst + 16 * nb + 4 * g4) = o[nb];
-    if (g4 == 0) {
-      part_ml[row * 2 + 0] = m_run;
-      part_ml[row * 2 + 1] = l_tot;
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = ok ? *(const u32x4*)(src + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
+        qf[ks] = __builtin_bit_cast(bf16x8, v);
+      }
     }
-  }
+    bt = block_table + (size_t)sp.s * max_blocks;
+    Kg = Kc + (size_t)sp.g * head_stride;
+    Vg = Vc + (size_t)sp.g * head_stride;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+
+    int t0 = t_begin;
+    load_k(t0, kr, live_r);
+    load_v(t0);
+    while (true) {
+      stage_v();
+      int t1 = t0 + kTok;
+      if (t1 < t_end) {
+        load_v(t1);
+        load_k(t1, kn, live_n);
+      }
+      compute_step(kr, live_r);
+      if (t1 >= t_end) break;
+      t0 = t1;
+      stage_v();
+      t1 = t0 + kTok;
+      if (t1 < t_end) {
+        load_v(t1);
+        load_k(t1, kr, live_r);
+      }
+      compute_step(kn, live_n);
+      if (t1 >= t_end) break;
+      t0 = t1;
+    }
+
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const int pair = sp.s * Hkv + sp.g;
+    const int id = w + pair;
+    if (qc < G) {
+      const size_t row = (size_t)id * G + qc;
+      float* dst = part_o + row * D;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) *(f32x4*)(dst + 16 * nb + 4 * g4) = o[nb];
+      if (g4 == 0) {
+        part_ml[row * 2 + 0] = m_run;
+        part_ml[row * 2 + 1] = l_tot;
+      }
+    }
+    if (lane == 0) {
+      if (seg.first) seg_first[pair] = id;
+      if (seg.last) seg_last[pair] = id;
+    }
+  } while (split_next(sp, ctx_lens, num_seqs, Hkv, max_context));
 }
 
 template <int D, typename OutT>
 __global__ __launch_bounds__(D) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int* __restrict__ seg_first, const int* __restrict__ seg_last,
     const int* __restrict__ ctx_lens, OutT* __restrict__ O, float* __restrict__ LSE,
-    int num_seqs, int Hq, int chunk_tokens, int max_context) {
+    int num_seqs, int Hq, int Hkv, int max_context, long long n_ids) {
   const int hq = blockIdx.x;
   const int s = blockIdx.y;
   const int n = threadIdx.x;
+  const int G = Hq / Hkv;
+  const int g = hq / G;
+  const int j = hq - g * G;
+  const int pair = s * Hkv + g;
   const int ctx = min(ctx_lens[s], max_context);
-  const int nc = ctx > 0 ? (ctx + chunk_tokens - 1) / chunk_tokens : 0;
-  // One pass over the chunks, kBatch at a time: all loads of a batch are
+  // The pair's partials are segments seg_first .. seg_last, written by the
+  // split waves of this call whenever the pair has a live token.
+  int first = 0, nc = 0;
+  bool bad = false;
+  if (ctx > 0) {
+    first = seg_first[pair];
+    const int last = seg_last[pair];
+    bad = first < 0 || last < first || (long long)last >= n_ids;
+    nc = bad ? 0 : last - first + 1;
+  }
+  // One pass over the partials, kBatch at a time: all loads of a batch are
   // issued before any is used (the partials are latency-bound, not
   // bandwidth-bound), then the running max absorbs the batch's max and the
   // sums are rescaled by 2^(old - new), as in the online softmax.
   constexpr int kBatch = 8;
-  const size_t stride = (size_t)num_seqs * Hq;
-  const size_t row0 = (size_t)s * Hq + hq;
   float big_m = -INFINITY, acc = 0.f, ell = 0.f;
   for (int c0 = 0; c0 < nc; c0 += kBatch) {
     float mv[kBatch], lv[kBatch], ov[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const bool ok = c0 + j < nc;
-      const size_t row = (size_t)(ok ? c0 + j : 0) * stride + row0;
-      mv[j] = ok ? part_ml[row * 2] : -INFINITY;
-      lv[j] = ok ? part_ml[row * 2 + 1] : 0.f;
-      ov[j] = ok ? part_o[row * D + n] : 0.f;
+    for (int k = 0; k < kBatch; ++k) {
+      const bool ok = c0 + k < nc;
+      const size_t row = (size_t)(first + (ok ? c0 + k : 0)) * G + j;
+      mv[k] = ok ? part_ml[row * 2] : -INFINITY;
+      lv[k] = ok ? part_ml[row * 2 + 1] : 0.f;
+      ov[k] = ok ? part_o[row * D + n] : 0.f;
     }
     float bm = big_m;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) bm = fmaxf(bm, mv[j]);
-    if (bm == -INFINITY) continue;  // every chunk so far saw no key
+    for (int k = 0; k < kBatch; ++k) bm = fmaxf(bm, mv[k]);
+    if (bm == -INFINITY) continue;  // every partial so far saw no key
     const float r = fast_exp2(big_m - bm);  // 0 while big_m is -inf
     acc *= r;
     ell *= r;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const float w = fast_exp2(mv[j] - bm);
-      ell += w * lv[j];
-      acc += w * ov[j];
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = fast_exp2(mv[k] - bm);
+      ell += w * lv[k];
+      acc += w * ov[k];
     }
     big_m = bm;
   }
   const float inv = ell > 0.f ? 1.f / ell : 0.f;
   const size_t orow = (size_t)s * Hq + hq;
-  O[orow * D + n] = (OutT)(acc * inv);
-  if (n == 0 && LSE) LSE[orow] = ell > 0.f ? (big_m + fast_log2(ell)) * kLn2 : -INFINITY;
+  // Segment ids out of range cannot come from the split kernel; NaN makes
+  // such a result impossible to mistake for attention output.
+  O[orow * D + n] = bad ? (OutT)NAN : (OutT)(acc * inv);
+  if (n == 0 && LSE)
+    LSE[orow] = bad ? NAN : ell > 0.f ? (big_m + fast_log2(ell)) * kLn2 : -INFINITY;
 }
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
+  const int G = a.Hq / a.Hkv;
+  const long long pairs = (long long)a.num_seqs * a.Hkv;
+  const long long n_ids = p.n_waves + pairs;
   float* part_o = (float*)a.workspace;
-  float* part_ml = part_o + (size_t)p.n_chunks_max * a.num_seqs * a.Hq * D;
-  if (p.n_chunks_max > 0) {
-    const int units = p.n_chunks_max * a.Hkv;
+  float* part_ml = part_o + (size_t)n_ids * G * D;
+  int* seg_first = (int*)(part_ml + (size_t)n_ids * G * 2);
+  int* seg_last = seg_first + pairs;
+  if (p.n_waves > 0) {
     const bool paged = a.block_size % 16 == 0;
     const int wg_waves = paged ? ETA_DECODE_WG_WAVES : 4;
-    // Every (sequence, chunk, KV head) slot the grid could need; the slots
-    // beyond the live work exit at once (and come last in launch order).
-    const long long slots = (long long)units * a.num_seqs;
-    dim3 grid((unsigned)((slots + wg_waves - 1) / wg_waves));
+    dim3 grid((unsigned)((p.n_waves + wg_waves - 1) / wg_waves));
     if (paged) {
       unsigned magic;
       int shift;
       page_magic(a.block_size, magic, shift);
       hipLaunchKernelGGL(decode_split_paged_kernel<D>, grid, dim3(64 * wg_waves), 0, stream,
                          (const __bf16*)a.Q, (const __bf16*)a.K_cache, (const __bf16*)a.V_cache,
-                         a.block_table, a.context_lens, part_o, part_ml, a.num_seqs, a.Hq, a.Hkv,
-                         a.Hq / a.Hkv, a.block_size, a.num_blocks, a.max_blocks_per_seq,
-                         a.max_context, p.chunk_tokens, p.n_chunks_max,
+                         a.block_table, a.context_lens, part_o, part_ml, seg_first, seg_last,
+                         a.num_seqs, a.Hq, a.Hkv, G, a.block_size, a.num_blocks,
+                         a.max_blocks_per_seq, a.max_context, p.steps_fixed, p.target_waves,
                          (long long)a.block_stride, (long long)a.token_stride,
                          (long long)a.head_stride, a.scale * kLog2e, magic, shift);
     } else {
       hipLaunchKernelGGL(decode_split_generic_kernel<D>, grid, dim3(64 * wg_waves), 0, stream,
                          (const __bf16*)a.Q, (const __bf16*)a.K_cache, (const __bf16*)a.V_cache,
-                         a.block_table, a.context_lens, part_o, part_ml, a.num_seqs, a.Hq, a.Hkv,
-                         a.Hq / a.Hkv, a.block_size, a.num_blocks, a.max_blocks_per_seq,
-                         a.max_context, p.chunk_tokens, p.n_chunks_max,
+                         a.block_table, a.context_lens, part_o, part_ml, seg_first, seg_last,
+                         a.num_seqs, a.Hq, a.Hkv, G, a.block_size, a.num_blocks,
+                         a.max_blocks_per_seq, a.max_context, p.steps_fixed, p.target_waves,
                          (long long)a.block_stride, (long long)a.token_stride,
                          (long long)a.head_stride, a.scale * kLog2e);
     }
@@ -625,15 +794,29 @@ hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t
   }
   dim3 mgrid((unsigned)a.Hq, (unsigned)a.num_seqs);
   hipLaunchKernelGGL((decode_merge_kernel<D, __bf16>), mgrid, dim3(D), 0, stream, part_o, part_ml,
-                     a.context_lens, (__bf16*)a.O, a.LSE, a.num_seqs, a.Hq, p.chunk_tokens,
-                     a.max_context);
+                     seg_first, seg_last, a.context_lens, (__bf16*)a.O, a.LSE, a.num_seqs, a.Hq,
+                     a.Hkv, a.max_context, n_ids);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t decode_workspace_bytes(int num_seqs, int Hq, int d, int n_chunks_max) {
-  return (size_t)n_chunks_max * num_seqs * Hq * ((size_t)d + 2) * sizeof(float);
+long long decode_split_waves(long long pairs, int d, int max_context, int steps_fixed) {
+  const long long u_max = pairs * ((max_context + kTok - 1) / kTok);
+  if (u_max <= 0) return 0;
+  if (steps_fixed > 0) return (u_max + steps_fixed - 1) / steps_fixed;
+  // The device's q >= ceil(U / target) and >= kDecodeMinSteps needs at most
+  // ceil(U / q) <= min(target, ceil(u_max / kDecodeMinSteps)) waves.
+  const long long target = decode_target_waves(d);
+  const long long cap = (u_max + kDecodeMinSteps - 1) / kDecodeMinSteps;
+  return target < cap ? target : cap;
+}
+
+size_t decode_workspace_bytes(long long pairs, int G, int d, long long n_waves) {
+  // Partials (d + 2 floats per query head) of every segment id, then the
+  // first and last segment id of every pair.
+  const long long rows = (n_waves + pairs) * G;
+  return (size_t)rows * ((size_t)d + 2) * sizeof(float) + (size_t)pairs * 2 * sizeof(int);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {

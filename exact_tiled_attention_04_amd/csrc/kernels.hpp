@@ -10,6 +10,8 @@ namespace eta {
 // A window side with no limit (larger than any sequence the library accepts).
 constexpr int kUnbounded = 1 << 30;
 
+constexpr int kNumCU = 256;  // MI355X compute units
+
 // Extra inputs of the forward's packed-ragged, paged and sparse modes
 // (all zero for dense rows).  Device pointers; sizes are host values.
 struct FwdSeqArgs {
@@ -113,10 +115,44 @@ struct DecodeArgs {
   void* workspace;
 };
 
+// Split plan of the paged decode.  The live 32-token steps of all (sequence,
+// KV head) pairs, laid end to end sequence-major, are cut into equal ranges
+// of q steps, one per split wave.  q is fixed by the caller (steps_fixed > 0,
+// at most kDecodeMaxSteps) or chosen on the device from the total step
+// count U, which only the device knows: q = max(ceil(U / target_waves),
+// kDecodeMinSteps).  The grid holds n_waves waves, enough for any U the
+// sizes allow; waves past ceil(U / q) exit at once.
+constexpr int kDecodeStepTokens = 32;
+constexpr int kDecodeMaxSteps = 127;  // 4064 tokens: block-table entries in 4 registers
+#ifndef ETA_DECODE_MIN_STEPS
+#define ETA_DECODE_MIN_STEPS 2
+#endif
+constexpr int kDecodeMinSteps = ETA_DECODE_MIN_STEPS;
 struct DecodePlan {
-  int chunk_tokens;
-  int n_chunks_max;
+  int steps_fixed;      // q when > 0
+  int target_waves;     // split waves of the automatic plan
+  long long n_waves;    // waves in the split grid
 };
+// Split waves of the automatic plan for head dimension d: one workgroup of
+// four waves per CU.  Measured over six batch shapes (64 x 4k-32k tokens,
+// 256 x 1k-4k, 16 x 32k-64k, 128 x 2k-16k with 2 KV heads, 32 x 8k, 8 x 1k-2k):
+// 2048 waves (all resident at 2 per SIMD) streamed 1-6% slower at d = 128,
+// 17% slower at d = 64; 1536 waves, which leave some CUs with two workgroups
+// and others with one, slower still; 768 (192 CUs busy) within 3% either
+// way; 512 8-15% slower.  Ranges of equal length gain nothing from uneven
+// CU loads, so the count is a multiple of the CU count.
+#ifndef ETA_DECODE_WAVES_D128
+#define ETA_DECODE_WAVES_D128 1024
+#endif
+#ifndef ETA_DECODE_WAVES_D64
+#define ETA_DECODE_WAVES_D64 1024
+#endif
+inline int decode_target_waves(int d) {
+  return d == 128 ? ETA_DECODE_WAVES_D128 : ETA_DECODE_WAVES_D64;
+}
+// Waves the split grid needs for pairs = num_seqs * Hkv pairs of at most
+// max_context tokens.
+long long decode_split_waves(long long pairs, int d, int max_context, int steps_fixed);
 
 struct BwdArgs {
   const void* Q;
@@ -138,7 +174,7 @@ struct BwdArgs {
 hipError_t launch_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
-size_t decode_workspace_bytes(int num_seqs, int Hq, int d, int n_chunks_max);
+size_t decode_workspace_bytes(long long pairs, int G, int d, long long n_waves);
 size_t bwd_workspace_bytes(int B, int H, int Nq, int d);
 
 }  // namespace eta

@@ -219,8 +219,9 @@ attn_status_t attn_fwd_block_sparse(const void* Q, const void* K, const void* V,
                                     attn_dtype_t dtype, void* stream);
 
 /*
- * Bytes of workspace attn_decode_paged needs for these sizes (0 when the
- * arguments are invalid).  chunk_tokens as for attn_decode_paged.
+ * Bytes of workspace attn_decode_paged needs for these sizes and any number
+ * of KV heads (0 when the arguments are invalid).  chunk_tokens as for
+ * attn_decode_paged.
  */
 size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_context,
                                         int chunk_tokens);
@@ -231,8 +232,11 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_con
  * decode need different kernels" and "Paged attention changes addressing":
  * token position pos of sequence s lives in physical block
  * block_table[s, pos / block_size] at slot pos % block_size; "Attention
- * kernels", FlashDecoding: the context is split into chunks whose partial
- * (o, m, l) are merged by max-rescaling.
+ * kernels", FlashDecoding: the context is split into pieces whose partial
+ * (o, m, l) are merged by max-rescaling.  The pieces are equal ranges of the
+ * contexts of all (sequence, KV head) pairs laid end to end in 32-token
+ * steps, one range per parallel work item, so a long context is split
+ * across items and an item may cover the ends of several short ones.
  *   Q            [num_seqs, Hq, d]                 device, bf16
  *   K_cache, V_cache: element (blk, slot, kvh, c) at
  *                blk*block_stride + slot*token_stride + kvh*head_stride + c
@@ -252,8 +256,9 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_con
  *                output or NULL.
  *   max_context  upper bound on context_lens (sizes the grid without reading
  *                device memory); must be <= max_blocks_per_seq*block_size.
- *   chunk_tokens context chunk per parallel work item, a positive multiple
- *                of 32 up to 4064, or 0 to let the library choose.
+ *   chunk_tokens tokens per parallel work item (its range of the steps laid
+ *                end to end), a positive multiple of 32 up to 4064, or 0 to
+ *                let the device choose from the actual context lengths.
  *   Hq % Hkv == 0 and Hq / Hkv <= 16; d in {64, 128}; dtype must be BF16;
  *   block_size >= 1; the strides must describe non-overlapping rows, all
  *   multiples of 8, in one of two page layouts:

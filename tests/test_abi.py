@@ -131,12 +131,21 @@ def test_workspace_queries(lib):
     # Backward: two floats (D and the base-2 LSE) per query row.
     assert attn.attn_bwd_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 2 * 4
     assert attn.attn_bwd_workspace_size(1, 1, 1, 96) == 0
-    # Decode: (d + 2) floats per (chunk, sequence, query head).
-    assert attn.attn_decode_paged_workspace_size(4, 8, 128, 1000, 256) == 4 * 4 * 8 * 130 * 4
+    # Decode: (d + 2) floats per query head of every segment (split wave +
+    # (sequence, KV head) pair), two ints per pair; the largest over the group
+    # sizes G = Hq / Hkv.  4 sequences, Hq = 8, 1000 tokens (32 steps), 256-token
+    # items (8 steps): G = 1 gives 32 pairs, 32 * 32 / 8 = 128 waves, 160 ids.
+    def ws(pairs, G, waves, d=128):
+        return (waves + pairs) * G * (d + 2) * 4 + pairs * 2 * 4
+    want = max(ws(4 * 8 // G, G, -(-(4 * 8 // G) * 32 // 8)) for G in (1, 2, 4, 8))
+    assert attn.attn_decode_paged_workspace_size(4, 8, 128, 1000, 256) == want == ws(32, 1, 128)
     assert attn.attn_decode_paged_workspace_size(4, 8, 128, 1000, 48) == 0
-    # The automatic chunk never needs more than the query reports.
+    # Automatic split: 1024 waves (one workgroup of four per CU); G = 16 needs
+    # the most rows here.
     auto = attn.attn_decode_paged_workspace_size(64, 32, 128, 32768, 0)
-    assert auto > 0
+    assert auto == max(ws(64 * 32 // G, G, 1024) for G in (1, 2, 4, 8, 16)) == ws(128, 16, 1024)
+    # Few steps: the range length never drops below 2 steps (64 tokens).
+    assert attn.attn_decode_paged_workspace_size(2, 2, 64, 100, 0) == ws(4, 1, 8, d=64)
 
 
 def test_plan_describe_per_phase(lib):

@@ -68,7 +68,8 @@ def test_block_sizes(gpu, block_size):
 
 @pytest.mark.parametrize("chunk", [32, 64, 96, 256, 1024, 0])
 def test_split_count_invariance(gpu, chunk):
-    """Any chunk size (any number of partials) gives the oracle's result."""
+    """Any work-item length (any number of partials per pair) gives the
+    oracle's result."""
     w = workloads.decode(num_seqs=6, Hq=32, Hkv=8, d=128, ctx_lo=900, ctx_hi=3000,
                          dtype="bf16", seed=7, poison_tail=True)
     scale = 1.0 / math.sqrt(128)
@@ -97,6 +98,51 @@ def test_many_sequences_with_empty_ones(gpu, block_size):
     assert torch.all(o[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
     check_out(to64(o), o_ref, "bf16")
     check_lse(to64(lse), lse_ref, "bf16")
+
+
+@pytest.mark.parametrize("block_size,chunk", [(16, 0), (16, 96), (8, 0), (32, 4064)])
+def test_split_ranges_cross_pairs(gpu, block_size, chunk):
+    """The split cuts the steps of all (sequence, KV head) pairs, laid end to
+    end, into equal ranges: one long context spread over many waves, short
+    and empty ones packed several to a wave, ranges starting and ending inside
+    pairs.  The automatic split (chunk 0) picks its range length on the device."""
+    rng = np.random.default_rng(41)
+    ctx = rng.integers(1, 120, size=90)
+    ctx[rng.random(90) < 0.2] = 0
+    ctx[[0, 5, 40, 64, 89]] = [9000, 0, 4097, 33, 2500]
+    w = workloads.decode(num_seqs=90, Hq=24, Hkv=8, d=128, ctx_lo=0, ctx_hi=0,
+                         context_lens=ctx.tolist(), block_size=block_size, dtype="bf16",
+                         seed=41, poison_tail=True)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = _decode(w, gpu, scale, chunk_tokens=chunk)
+    o_ref, lse_ref = _oracle(w, scale)
+    empty = torch.from_numpy(ctx == 0)
+    assert torch.all(o[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
+    check_out(to64(o), o_ref, "bf16")
+    check_lse(to64(lse), lse_ref, "bf16")
+
+
+def test_reused_workspace_other_contexts(gpu):
+    """A workspace left by a call with other context lengths (pairs that were
+    empty become live and the reverse) gives the oracle's result: the merge
+    reads only what this call's split wrote."""
+    ctx_a = [0, 700, 33, 0, 1500, 64]
+    ctx_b = [900, 0, 31, 2000, 1, 0]
+    ws = torch.empty(attn.attn_decode_paged_workspace_size(6, 16, 128, 2048, 64) + 16,
+                     dtype=torch.uint8, device=gpu)
+    scale = 1.0 / math.sqrt(128)
+    for ctx, seed in ((ctx_a, 51), (ctx_b, 52)):
+        w = workloads.decode(num_seqs=6, Hq=16, Hkv=4, d=128, ctx_lo=0, ctx_hi=0,
+                             context_lens=ctx, dtype="bf16", seed=seed, poison_tail=True,
+                             max_blocks_per_seq=128)
+        g = _to_gpu(w, gpu)
+        o, lse = attn.attn_decode_paged(g["q"], g["k_cache"], g["v_cache"], g["block_table"],
+                                        g["context_lens"], scale, 2048, chunk_tokens=64,
+                                        workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = _oracle(w, scale)
+        check_out(to64(o.cpu()), o_ref, "bf16")
+        check_lse(to64(lse.cpu()), lse_ref, "bf16")
 
 
 def test_empty_and_clamped_contexts(gpu):
