@@ -115,7 +115,6 @@ attn_status_t check_decode_shape(int num_seqs, int Hq, int Hkv, int d, int block
                 "max_blocks_per_seq=%d max_context=%d)",
                 num_seqs, Hq, Hkv, block_size, num_blocks, max_blocks_per_seq, max_context);
   if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
-  if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
   if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension %d not in {64,128}", d);
   if ((long long)max_context > (long long)max_blocks_per_seq * block_size)
     return fail(ATTN_ERR_INVALID_ARG, "max_context=%d exceeds block table capacity %lld",
@@ -459,7 +458,7 @@ attn_status_t attn_fwd_splitkv(const void* Q, const void* K, const void* V, void
 
 // Workspace of a decode with Hkv = Hq / G KV heads.
 size_t decode_ws_for(int num_seqs, int Hq, int G, int d, int max_context, int chunk_tokens) {
-  const long long pairs = (long long)num_seqs * (Hq / G);
+  const long long pairs = eta::decode_pairs(num_seqs, Hq / G, G);
   const long long waves = eta::decode_split_waves(pairs, d, max_context, chunk_tokens / 32);
   return eta::decode_workspace_bytes(pairs, G, d, waves);
 }
@@ -472,7 +471,7 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_con
   // The size depends on the group size G = Hq / Hkv, which the caller has
   // not given: cover every G the decode accepts.
   size_t most = 0;
-  for (int G = 1; G <= 16 && G <= Hq; ++G)
+  for (int G = 1; G <= Hq; ++G)
     if (Hq % G == 0) {
       const size_t b = decode_ws_for(num_seqs, Hq, G, d, max_context, chunk_tokens);
       if (b > most) most = b;
@@ -514,7 +513,7 @@ attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* 
   if (block_stride >= (1LL << 30))
     return fail(ATTN_ERR_UNSUPPORTED, "block_stride=%lld elements exceeds 2^30",
                 (long long)block_stride);
-  const long long pairs = (long long)num_seqs * Hkv;
+  const long long pairs = eta::decode_pairs(num_seqs, Hkv, Hq / Hkv);
   const long long n_waves = eta::decode_split_waves(pairs, d, max_context, chunk_tokens / 32);
   // Segment ids (split wave + pair index) and the split grid stay in int.
   if (n_waves + pairs > kMaxGrid)
@@ -581,7 +580,8 @@ int attn_plan_describe(int phase, int B, int H, int Hkv, int Nq, int Nk, int d, 
     if (check_decode_shape(B, H, Hkv, d, 16, 1, (Nk + 15) / 16 > 0 ? (Nk + 15) / 16 : 1, Nk, 0) !=
         ATTN_OK)
       return -1;
-    const long long waves = eta::decode_split_waves((long long)B * Hkv, d, Nk, 0);
+    const long long waves =
+        eta::decode_split_waves(eta::decode_pairs(B, Hkv, H / Hkv), d, Nk, 0);
     n = snprintf(tmp, sizeof(tmp),
                  "phase=decode kernel=decode_split_mfma16x16x32+decode_merge d=%d G=%d "
                  "split=balanced (equal 32-token step ranges of all seq x KV-head pairs, "

@@ -16,8 +16,9 @@
 // kernels.hpp), so every wave streams the same number of cache bytes and a
 // wave whose range crosses a pair boundary writes one partial per pair it
 // touches.  Within a pair, the G query heads of the group are the columns
-// of a 16x16x32 MFMA (G <= 16), so every K and V byte is read from HBM once
-// and used by all G heads.  Per 32 tokens
+// of a 16x16x32 MFMA, so every K and V byte is read from HBM once and used
+// by all G heads; a group of more than 16 heads is split into pairs of 16
+// (each reading the KV head again).  Per 32 tokens
 // (two 16-token groups): K and V arrive as whole rows, several per load.  On
 // the path for block sizes that are multiples of 16 (wave-uniform page
 // addressing through buffer resources), K rows are staged in a wave-private
@@ -94,8 +95,9 @@ __device__ __forceinline__ long long uniform64(long long v) {
   return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
-// Where a split wave's work starts.  Pair (s, g) owns steps
-// [seq_base(s) + g n_s, seq_base(s) + (g + 1) n_s), n_s = ceil(ctx_s / 32);
+// Where a split wave's work starts.  Pair g of sequence s (one of `units`
+// per sequence) owns steps [seq_base(s) + g n_s, seq_base(s) + (g + 1) n_s),
+// n_s = ceil(ctx_s / 32);
 // wave w takes steps [w q, min((w + 1) q, U)).  The wave reads the
 // sequences' contexts 64 at a time (one per lane): a reduction gives U, and
 // with it q when the caller left it open; an inclusive scan finds the
@@ -103,19 +105,19 @@ __device__ __forceinline__ long long uniform64(long long v) {
 struct SplitPos {
   long long a, b;      // the wave's steps [a, b)
   long long seq_base;  // first step of sequence s
-  int s, n, ctx, g;    // sequence, its steps, its context, KV head
+  int s, n, ctx, g;    // sequence, its steps, its context, pair within it
 };
 
 // False when the wave has no steps.
 __device__ __forceinline__ bool split_start(int w, const int* __restrict__ ctx_lens, int num_seqs,
-                                            int Hkv, int max_context, int steps_fixed,
+                                            int units, int max_context, int steps_fixed,
                                             int target_waves, int lane, SplitPos& sp) {
   auto ctx_of = [&](int sq) -> int {
     return sq < num_seqs ? max(0, min(ctx_lens[sq], max_context)) : 0;
   };
   long long U = 0;
   for (int base = 0; base < num_seqs; base += 64) {
-    long long c = (long long)ctx_steps(ctx_of(base + lane)) * Hkv;
+    long long c = (long long)ctx_steps(ctx_of(base + lane)) * units;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
     U += c;
@@ -134,7 +136,7 @@ __device__ __forceinline__ bool split_start(int w, const int* __restrict__ ctx_l
   for (int base = 0; base < num_seqs; base += 64) {
     const int ctx = ctx_of(base + lane);
     const int n = ctx_steps(ctx);
-    const long long c = (long long)n * Hkv;
+    const long long c = (long long)n * units;
     long long incl = c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -176,13 +178,13 @@ __device__ __forceinline__ SplitSeg split_segment(const SplitPos& sp) {
   return sg;
 }
 __device__ __forceinline__ bool split_next(SplitPos& sp, const int* __restrict__ ctx_lens,
-                                           int num_seqs, int Hkv, int max_context) {
+                                           int num_seqs, int units, int max_context) {
   const long long P = sp.seq_base + (long long)sp.g * sp.n;
   sp.a = sp.b - P < sp.n ? sp.b : P + sp.n;
   if (sp.a >= sp.b) return false;
-  if (++sp.g < Hkv) return true;
+  if (++sp.g < units) return true;
   sp.g = 0;
-  sp.seq_base += (long long)sp.n * Hkv;
+  sp.seq_base += (long long)sp.n * units;
   do {
     if (++sp.s >= num_seqs) return false;  // not reached: steps remain
     sp.ctx = max(0, min(ctx_lens[sp.s], max_context));
@@ -221,9 +223,16 @@ void decode_split_paged_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int w = blockIdx.x * ETA_DECODE_WG_WAVES + wave;
   SplitPos sp;
-  if (!split_start(w, ctx_lens, num_seqs, Hkv, max_context, steps_fixed, target_waves, lane, sp))
+  // A group of G > 16 query heads is split into subgroups of 16 (the MFMA
+  // columns); each (KV head, subgroup) is a pair of its own, re-reading the
+  // KV head's cache rows.
+  const int nsg = (G + 15) >> 4;
+  const int units = Hkv * nsg;     // pairs per sequence
+  const int gs = G < 16 ? G : 16;  // partial rows per segment
+  if (!split_start(w, ctx_lens, num_seqs, units, max_context, steps_fixed, target_waves, lane, sp))
     return;
   int t_begin = 0, t_end = 0;  // the current piece's tokens of pair (sp.s, sp.g)
+  int kvh = 0;                 // the pair's KV head
 
   __bf16* vs = vs_all[wave];
   __bf16* kst = ks_all[wave];
@@ -266,7 +275,7 @@ void decode_split_paged_kernel(
       if (ph < 0 || ph >= num_blocks) live = 0;
       else
         base = (long long)ph * block_stride + (long long)slot0 * token_stride +
-               (long long)sp.g * head_stride;
+               (long long)kvh * head_stride;
     }
     live = __builtin_amdgcn_readfirstlane(live);
     const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)base);
@@ -401,9 +410,13 @@ void decode_split_paged_kernel(
   };
   do {
     const SplitSeg seg = split_segment(sp);
+    kvh = sp.g / nsg;
+    const int sub = sp.g - kvh * nsg;
+    const int heads = min(16, G - 16 * sub);  // query heads of this pair
     {
-      const bool ok = qc < G;
-      const __bf16* src = Q + ((size_t)sp.s * Hq + (size_t)sp.g * G + (ok ? qc : 0)) * D;
+      const bool ok = qc < heads;
+      const __bf16* src =
+          Q + ((size_t)sp.s * Hq + (size_t)kvh * G + 16 * sub + (ok ? qc : 0)) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 v = ok ? *(const u32x4*)(src + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
@@ -456,10 +469,10 @@ void decode_split_paged_kernel(
     // segments (both w and the pair index only grow along the steps).
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot = halves_sum(l_tot);
-    const int pair = sp.s * Hkv + sp.g;
+    const int pair = sp.s * units + sp.g;
     const int id = w + pair;
-    if (qc < G) {
-      const size_t row = (size_t)id * G + qc;
+    if (qc < heads) {
+      const size_t row = (size_t)id * gs + qc;
       float* dst = part_o + row * D;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) *(f32x4*)(dst + 16 * nb + 4 * g4) = o[nb];
@@ -472,7 +485,7 @@ void decode_split_paged_kernel(
       if (seg.first) seg_first[pair] = id;
       if (seg.last) seg_last[pair] = id;
     }
-  } while (split_next(sp, ctx_lens, num_seqs, Hkv, max_context));
+  } while (split_next(sp, ctx_lens, num_seqs, units, max_context));
 }
 
 // Generic block sizes: every token's page is looked up on its own lane.
@@ -496,9 +509,16 @@ void decode_split_generic_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int w = blockIdx.x * 4 + wave;
   SplitPos sp;
-  if (!split_start(w, ctx_lens, num_seqs, Hkv, max_context, steps_fixed, target_waves, lane, sp))
+  // A group of G > 16 query heads is split into subgroups of 16 (the MFMA
+  // columns); each (KV head, subgroup) is a pair of its own, re-reading the
+  // KV head's cache rows.
+  const int nsg = (G + 15) >> 4;
+  const int units = Hkv * nsg;     // pairs per sequence
+  const int gs = G < 16 ? G : 16;  // partial rows per segment
+  if (!split_start(w, ctx_lens, num_seqs, units, max_context, steps_fixed, target_waves, lane, sp))
     return;
   int t_begin = 0, t_end = 0;  // the current segment's tokens of pair (sp.s, sp.g)
+  int kvh = 0;                 // the pair's KV head
 
   __bf16* vs = vs_all[wave];
   const int qc = lane & 15;   // query column (head within the group) / A row
@@ -630,9 +650,13 @@ void decode_split_generic_kernel(
     const SplitSeg seg = split_segment(sp);
     t_begin = seg.t_begin;
     t_end = seg.t_end;
+    kvh = sp.g / nsg;
+    const int sub = sp.g - kvh * nsg;
+    const int heads = min(16, G - 16 * sub);  // query heads of this pair
     {
-      const bool ok = qc < G;
-      const __bf16* src = Q + ((size_t)sp.s * Hq + (size_t)sp.g * G + (ok ? qc : 0)) * D;
+      const bool ok = qc < heads;
+      const __bf16* src =
+          Q + ((size_t)sp.s * Hq + (size_t)kvh * G + 16 * sub + (ok ? qc : 0)) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 v = ok ? *(const u32x4*)(src + 32 * ks + 8 * g4) : u32x4{0, 0, 0, 0};
@@ -640,8 +664,8 @@ void decode_split_generic_kernel(
       }
     }
     bt = block_table + (size_t)sp.s * max_blocks;
-    Kg = Kc + (size_t)sp.g * head_stride;
-    Vg = Vc + (size_t)sp.g * head_stride;
+    Kg = Kc + (size_t)kvh * head_stride;
+    Vg = Vc + (size_t)kvh * head_stride;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run = -INFINITY;
@@ -673,10 +697,10 @@ void decode_split_generic_kernel(
 
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
-    const int pair = sp.s * Hkv + sp.g;
+    const int pair = sp.s * units + sp.g;
     const int id = w + pair;
-    if (qc < G) {
-      const size_t row = (size_t)id * G + qc;
+    if (qc < heads) {
+      const size_t row = (size_t)id * gs + qc;
       float* dst = part_o + row * D;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) *(f32x4*)(dst + 16 * nb + 4 * g4) = o[nb];
@@ -689,7 +713,7 @@ void decode_split_generic_kernel(
       if (seg.first) seg_first[pair] = id;
       if (seg.last) seg_last[pair] = id;
     }
-  } while (split_next(sp, ctx_lens, num_seqs, Hkv, max_context));
+  } while (split_next(sp, ctx_lens, num_seqs, units, max_context));
 }
 
 template <int D, typename OutT>
@@ -702,9 +726,11 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
   const int s = blockIdx.y;
   const int n = threadIdx.x;
   const int G = Hq / Hkv;
+  const int nsg = (G + 15) >> 4;
+  const int gs = G < 16 ? G : 16;
   const int g = hq / G;
   const int j = hq - g * G;
-  const int pair = s * Hkv + g;
+  const int pair = (s * Hkv + g) * nsg + (j >> 4);
   const int ctx = min(ctx_lens[s], max_context);
   // The pair's partials are segments seg_first .. seg_last, written by the
   // split waves of this call whenever the pair has a live token.
@@ -727,7 +753,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const bool ok = c0 + k < nc;
-      const size_t row = (size_t)(first + (ok ? c0 + k : 0)) * G + j;
+      const size_t row = (size_t)(first + (ok ? c0 + k : 0)) * gs + (j & 15);
       mv[k] = ok ? part_ml[row * 2] : -INFINITY;
       lv[k] = ok ? part_ml[row * 2 + 1] : 0.f;
       ov[k] = ok ? part_o[row * D + n] : 0.f;
@@ -759,11 +785,12 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
-  const long long pairs = (long long)a.num_seqs * a.Hkv;
+  const int gs = G < 16 ? G : 16;
+  const long long pairs = decode_pairs(a.num_seqs, a.Hkv, G);
   const long long n_ids = p.n_waves + pairs;
   float* part_o = (float*)a.workspace;
-  float* part_ml = part_o + (size_t)n_ids * G * D;
-  int* seg_first = (int*)(part_ml + (size_t)n_ids * G * 2);
+  float* part_ml = part_o + (size_t)n_ids * gs * D;
+  int* seg_first = (int*)(part_ml + (size_t)n_ids * gs * 2);
   int* seg_last = seg_first + pairs;
   if (p.n_waves > 0) {
     const bool paged = a.block_size % 16 == 0;
@@ -813,9 +840,9 @@ long long decode_split_waves(long long pairs, int d, int max_context, int steps_
 }
 
 size_t decode_workspace_bytes(long long pairs, int G, int d, long long n_waves) {
-  // Partials (d + 2 floats per query head) of every segment id, then the
-  // first and last segment id of every pair.
-  const long long rows = (n_waves + pairs) * G;
+  // Partials (d + 2 floats per query head of a pair) of every segment id,
+  // then the first and last segment id of every pair.
+  const long long rows = (n_waves + pairs) * (G < 16 ? G : 16);
   return (size_t)rows * ((size_t)d + 2) * sizeof(float) + (size_t)pairs * 2 * sizeof(int);
 }
 

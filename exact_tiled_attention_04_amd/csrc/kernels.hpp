@@ -150,8 +150,12 @@ struct DecodePlan {
 inline int decode_target_waves(int d) {
   return d == 128 ? ETA_DECODE_WAVES_D128 : ETA_DECODE_WAVES_D64;
 }
-// Waves the split grid needs for pairs = num_seqs * Hkv pairs of at most
-// max_context tokens.
+// (sequence, KV head, subgroup of at most 16 query heads) pairs of a decode.
+inline long long decode_pairs(int num_seqs, int Hkv, int G) {
+  return (long long)num_seqs * Hkv * ((G + 15) / 16);
+}
+// Waves the split grid needs for that many pairs of at most max_context
+// tokens.
 long long decode_split_waves(long long pairs, int d, int max_context, int steps_fixed);
 
 struct BwdArgs {

@@ -259,7 +259,9 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_con
  *   chunk_tokens tokens per parallel work item (its range of the steps laid
  *                end to end), a positive multiple of 32 up to 4064, or 0 to
  *                let the device choose from the actual context lengths.
- *   Hq % Hkv == 0 and Hq / Hkv <= 16; d in {64, 128}; dtype must be BF16;
+ *   Hq % Hkv == 0 (a group of G = Hq / Hkv > 16 query heads is processed as
+ *   subgroups of 16, each reading its KV head's cache rows once); d in
+ *   {64, 128}; dtype must be BF16;
  *   block_size >= 1; the strides must describe non-overlapping rows, all
  *   multiples of 8, in one of two page layouts:
  *     token-major [block, slot, head, d]: head_stride >= d,

@@ -93,7 +93,6 @@ def _decode(lib, q=FAKE, ws=FAKE, ws_bytes=1 << 30, num_seqs=2, Hq=8, Hkv=2, d=1
     (dict(q=NULL), attn.ATTN_ERR_INVALID_ARG),
     (dict(num_seqs=0), attn.ATTN_ERR_INVALID_ARG),
     (dict(Hq=6, Hkv=4), attn.ATTN_ERR_INVALID_ARG),
-    (dict(Hq=34, Hkv=2), attn.ATTN_ERR_UNSUPPORTED),   # 17 query heads per KV head
     (dict(d=80), attn.ATTN_ERR_UNSUPPORTED),
     (dict(max_context=65), attn.ATTN_ERR_INVALID_ARG),  # beyond 4 blocks x 16
     (dict(chunk=48), attn.ATTN_ERR_INVALID_ARG),
@@ -144,6 +143,10 @@ def test_workspace_queries(lib):
     # the most rows here.
     auto = attn.attn_decode_paged_workspace_size(64, 32, 128, 32768, 0)
     assert auto == max(ws(64 * 32 // G, G, 1024) for G in (1, 2, 4, 8, 16)) == ws(128, 16, 1024)
+    # A group of more than 16 query heads is split into pairs of 16 heads:
+    # Hq = 34 = 17 x 2 (G = 34: one KV head, three pairs of 16, 16 and 2 heads).
+    pairs34 = 3
+    assert attn.attn_decode_paged_workspace_size(1, 34, 128, 64, 32) >= ws(pairs34, 16, 2)
     # Few steps: the range length never drops below 2 steps (64 tokens).
     assert attn.attn_decode_paged_workspace_size(2, 2, 64, 100, 0) == ws(4, 1, 8, d=64)
 

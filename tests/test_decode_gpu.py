@@ -122,6 +122,23 @@ def test_split_ranges_cross_pairs(gpu, block_size, chunk):
     check_lse(to64(lse), lse_ref, "bf16")
 
 
+@pytest.mark.parametrize("d,Hq,Hkv,block_size", [(128, 32, 1, 16), (128, 48, 2, 16),
+                                                 (64, 40, 2, 16), (128, 24, 1, 8)])
+def test_groups_above_16_heads(gpu, d, Hq, Hkv, block_size):
+    """Groups of more than 16 query heads per KV head (multi-query 32:1, 24:1,
+    20:1): subgroups of 16 heads are pairs of their own in the split."""
+    ctx = [1, 17, 300, 1000, 0, 2049, 64]
+    w = workloads.decode(num_seqs=len(ctx), Hq=Hq, Hkv=Hkv, d=d, ctx_lo=0, ctx_hi=0,
+                         context_lens=ctx, block_size=block_size, dtype="bf16",
+                         seed=Hq + d + block_size, poison_tail=True)
+    scale = 1.0 / math.sqrt(d)
+    for chunk in (0, 64):
+        o, lse = _decode(w, gpu, scale, chunk_tokens=chunk)
+        o_ref, lse_ref = _oracle(w, scale)
+        check_out(to64(o), o_ref, "bf16")
+        check_lse(to64(lse), lse_ref, "bf16")
+
+
 def test_reused_workspace_other_contexts(gpu):
     """A workspace left by a call with other context lengths (pairs that were
     empty become live and the reverse) gives the oracle's result: the merge
