@@ -323,6 +323,9 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, scale, max
     elements, with ``cache_dims`` = (num_blocks, block_size, Hkv) when the
     tensor's shape is not [blocks, slots, heads, d]); block_table int32
     [num_seqs, max_blocks]; context_lens int32 [num_seqs] on the device.
+    ``chunk_tokens`` > 0 fixes the tokens per split work item (a multiple of
+    32 up to 4064); 0 lets the device cut the contexts of all (sequence, KV
+    head) pairs, laid end to end, into equal ranges.
     """
     lib = load_library()
     _need_device(q, k_cache, v_cache, block_table, context_lens)
