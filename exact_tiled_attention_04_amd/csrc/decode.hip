@@ -716,15 +716,23 @@ void decode_split_generic_kernel(
   } while (split_next(sp, ctx_lens, num_seqs, units, max_context));
 }
 
-template <int D, typename OutT>
-__global__ __launch_bounds__(D) void decode_merge_kernel(
+// Thread groups per merge workgroup: with PARTS > 1 a pair's partials are
+// dealt out to PARTS groups of D threads and their results combined through
+// LDS, so a pair with many partials (few, long contexts) takes 1/PARTS of
+// the dependent load rounds.  The launcher picks PARTS = 4 when the split
+// gives at least 16 waves per pair: with fewer partials per pair the extra
+// waves and the LDS step cost more than they save (measured: one 64k
+// context +22%, 4 x 4k-8k +10%; 32 x 1k -7% with four groups).
+template <int D, int PARTS, typename OutT>
+__global__ __launch_bounds__(D * PARTS) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int* __restrict__ seg_first, const int* __restrict__ seg_last,
     const int* __restrict__ ctx_lens, OutT* __restrict__ O, float* __restrict__ LSE,
     int num_seqs, int Hq, int Hkv, int max_context, long long n_ids) {
   const int hq = blockIdx.x;
   const int s = blockIdx.y;
-  const int n = threadIdx.x;
+  const int n = threadIdx.x % D;
+  const int part = threadIdx.x / D;
   const int G = Hq / Hkv;
   const int nsg = (G + 15) >> 4;
   const int gs = G < 16 ? G : 16;
@@ -742,18 +750,21 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
     bad = first < 0 || last < first || (long long)last >= n_ids;
     nc = bad ? 0 : last - first + 1;
   }
-  // One pass over the partials, kBatch at a time: all loads of a batch are
-  // issued before any is used (the partials are latency-bound, not
-  // bandwidth-bound), then the running max absorbs the batch's max and the
-  // sums are rescaled by 2^(old - new), as in the online softmax.
+  // Group `part` takes partials part, part + PARTS, ..., kBatch at a
+  // time: all loads of a batch are issued before any is used (the partials
+  // are latency-bound, not bandwidth-bound), then the running max absorbs
+  // the batch's max and the sums are rescaled by 2^(old - new), as in the
+  // online softmax.
   constexpr int kBatch = 8;
+  const size_t row0 = (size_t)first * gs + (j & 15);
   float big_m = -INFINITY, acc = 0.f, ell = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += kBatch) {
+  for (int c0 = part; c0 < nc; c0 += kBatch * PARTS) {
     float mv[kBatch], lv[kBatch], ov[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const bool ok = c0 + k < nc;
-      const size_t row = (size_t)(first + (ok ? c0 + k : 0)) * gs + (j & 15);
+      const int c = c0 + k * PARTS;
+      const bool ok = c < nc;
+      const size_t row = row0 + (size_t)(ok ? c : 0) * gs;
       mv[k] = ok ? part_ml[row * 2] : -INFINITY;
       lv[k] = ok ? part_ml[row * 2 + 1] : 0.f;
       ov[k] = ok ? part_o[row * D + n] : 0.f;
@@ -773,13 +784,36 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
     }
     big_m = bm;
   }
+  float M = big_m;
+  if constexpr (PARTS > 1) {
+    // The groups' (m, acc, l) combined by the same rescaling.
+    __shared__ float sm_m[PARTS][D], sm_a[PARTS][D], sm_l[PARTS][D];
+    sm_m[part][n] = big_m;
+    sm_a[part][n] = acc;
+    sm_l[part][n] = ell;
+    __syncthreads();
+    if (part != 0) return;
+    M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < PARTS; ++p) M = fmaxf(M, sm_m[p][n]);
+    acc = 0.f;
+    ell = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int p = 0; p < PARTS; ++p) {
+        const float w = fast_exp2(sm_m[p][n] - M);  // 0 for a group that saw no key
+        acc += w * sm_a[p][n];
+        ell += w * sm_l[p][n];
+      }
+    }
+  }
   const float inv = ell > 0.f ? 1.f / ell : 0.f;
   const size_t orow = (size_t)s * Hq + hq;
   // Segment ids out of range cannot come from the split kernel; NaN makes
   // such a result impossible to mistake for attention output.
   O[orow * D + n] = bad ? (OutT)NAN : (OutT)(acc * inv);
   if (n == 0 && LSE)
-    LSE[orow] = bad ? NAN : ell > 0.f ? (big_m + fast_log2(ell)) * kLn2 : -INFINITY;
+    LSE[orow] = bad ? NAN : ell > 0.f ? (M + fast_log2(ell)) * kLn2 : -INFINITY;
 }
 
 template <int D>
@@ -820,9 +854,14 @@ hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t
     if (e != hipSuccess) return e;
   }
   dim3 mgrid((unsigned)a.Hq, (unsigned)a.num_seqs);
-  hipLaunchKernelGGL((decode_merge_kernel<D, __bf16>), mgrid, dim3(D), 0, stream, part_o, part_ml,
-                     seg_first, seg_last, a.context_lens, (__bf16*)a.O, a.LSE, a.num_seqs, a.Hq,
-                     a.Hkv, a.max_context, n_ids);
+  if (p.n_waves >= 16 * pairs)
+    hipLaunchKernelGGL((decode_merge_kernel<D, 4, __bf16>), mgrid, dim3(D * 4), 0, stream,
+                       part_o, part_ml, seg_first, seg_last, a.context_lens, (__bf16*)a.O, a.LSE,
+                       a.num_seqs, a.Hq, a.Hkv, a.max_context, n_ids);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<D, 1, __bf16>), mgrid, dim3(D), 0, stream, part_o,
+                       part_ml, seg_first, seg_last, a.context_lens, (__bf16*)a.O, a.LSE,
+                       a.num_seqs, a.Hq, a.Hkv, a.max_context, n_ids);
   return hipGetLastError();
 }
 
