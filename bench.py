@@ -466,7 +466,8 @@ def sweep(args, dev, stream):
     # Decode: sequences, context length, GQA group, cache block size.
     for S, Hq, Hkv, lo, hi, bs in [(64, 32, 8, 4096, 32768, 16), (64, 32, 8, 4096, 32768, 32),
                                    (16, 32, 8, 32768, 65536, 16), (256, 32, 8, 1024, 4096, 16),
-                                   (64, 64, 8, 8192, 16384, 16), (128, 16, 16, 2048, 8192, 16)]:
+                                   (64, 64, 8, 8192, 16384, 16), (128, 16, 16, 2048, 8192, 16),
+                                   (1, 32, 8, 65536, 65536, 16), (8, 32, 1, 1024, 2048, 16)]:
         w = workloads.decode(num_seqs=S, Hq=Hq, Hkv=Hkv, d=128, ctx_lo=lo, ctx_hi=hi,
                              block_size=bs, max_blocks_per_seq=(hi + bs - 1) // bs,
                              dtype="bf16", seed=3, device=str(dev))
