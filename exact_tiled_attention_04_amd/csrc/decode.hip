@@ -79,7 +79,7 @@ static_assert(kDecodeMaxSteps * kTok <= 4064, "piece block-table entries exceed 
 // one page, so its location is wave-uniform.  A group is addressed through a
 // raw buffer resource whose base is the group's first cache row and whose
 // range ends after its last live token (zero when the group is past the
-// chunk or its block-table entry lies outside the cache): K and V rows past
+// piece or its block-table entry lies outside the cache): K and V rows past
 // the context, or of a bad page, arrive as zeros with no branches, and the
 // score mask is a compare with the group's live-token count.
 #ifndef ETA_DECODE_WG_WAVES
@@ -252,7 +252,7 @@ void decode_split_paged_kernel(
   int bt_base = 0;
   int bt_r[4];
   auto page_of = [&](int logical) -> int {
-    const int idx = logical - bt_base;  // 0 <= idx < 256 by the chunk limit
+    const int idx = logical - bt_base;  // 0 <= idx < 256 by the piece limit
     const int r = idx >> 6, l = idx & 63;
     const int v = r == 0 ? bt_r[0] : r == 1 ? bt_r[1] : r == 2 ? bt_r[2] : bt_r[3];
     return __builtin_amdgcn_readlane(v, l);
@@ -260,7 +260,7 @@ void decode_split_paged_kernel(
 
   struct Group {
     buf_rsrc k, v;
-    int live;  // tokens of the group inside the chunk (0 if none or bad page)
+    int live;  // tokens of the group inside the piece (0 if none or bad page)
   };
   // Everything about a group is wave-uniform; readfirstlane makes that
   // visible to the compiler so the buffer resources live in SGPRs.
@@ -531,7 +531,7 @@ void decode_split_generic_kernel(
   const __bf16* Vg = Vc;
 
   // Address of token `pos` of this sequence, or null when pos is past the
-  // chunk or its block-table entry lies outside the cache.
+  // segment or its block-table entry lies outside the cache.
   auto tok_ptr = [&](const __bf16* base, int pos) -> const __bf16* {
     if (pos >= t_end) return nullptr;
     const int logical = pos / block_size;
