@@ -156,26 +156,69 @@ def _need_device(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+# The C ABI sees only pointers, so every extent the kernels rely on is
+# checked here, before any launch: a mis-shaped tensor would otherwise be
+# read or written past its end.
+
+def _need_shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_dtype(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _need_dims(t, n, name):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got {t.dim()}")
+
+
+def _out_lse(out, lse, o_shape, lse_shape, dtype, device):
+    """Caller-supplied outputs are checked against the result's extents;
+    missing ones are allocated."""
+    if out is None:
+        out = torch.empty(o_shape, dtype=dtype, device=device)
+    _need_shape(out, o_shape, "out")
+    _need_dtype(out, dtype, "out")
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=device)
+    _need_shape(lse, lse_shape, "lse")
+    _need_dtype(lse, torch.float32, "lse")
+    return out, lse
+
+
 def _fwd_args(q, k, v, out, lse):
-    _need_device(q, k, v)
+    _need_dims(q, 4, "q")
+    _need_dims(k, 4, "k")
     B, H, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B, Hkv, Nk, d]")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    _need_device(out, lse)
+    out, lse = _out_lse(out, lse, (B, H, Nq, d), (B, H, Nq), q.dtype, q.device)
+    _need_device(q, k, v, out, lse)
     return (B, H, Hkv, Nq, Nk, d), out, lse
 
 
-def attn_fwd(q, k, v, scale, causal, out=None, lse=None, stream=None):
-    """O, LSE = attention(q, k, v).  q [B,H,Nq,d]; k, v [B,Hkv,Nk,d]."""
+def attn_fwd(q, k, v, scale, causal, out=None, lse=None, stream=None, workspace=None):
+    """O, LSE = attention(q, k, v).  q [B,H,Nq,d]; k, v [B,Hkv,Nk,d].
+
+    bf16 grids too small to fill the GPU ("Modern attention kernels", "Work
+    partitioning in FlashAttention-2") go through the key-split entry point
+    attn_fwd_splitkv, with a workspace of the size the library asks for
+    (``workspace`` if given, else allocated here); other calls go to the C
+    ABI's attn_fwd, which needs no workspace."""
     lib = load_library()
     dims, out, lse = _fwd_args(q, k, v, out, lse)
+    if q.dtype == torch.bfloat16:
+        B, H, _, Nq, Nk, d = dims
+        right = 0 if causal else -1
+        if attn_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, -1, right, 0) > 0:
+            return attn_fwd_splitkv(q, k, v, scale, -1, right, 0, out=out, lse=lse,
+                                    workspace=workspace, stream=stream)
     _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *dims, float(scale),
                         int(bool(causal)), _dtype_code(q), _stream(stream)))
     return out, lse
@@ -211,6 +254,8 @@ def attn_fwd_splitkv(q, k, v, scale, window_left=-1, window_right=-1, chunk_keys
                                            chunk_keys)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need_workspace(workspace, need)
     _check(lib.attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), *dims,
                                 float(scale), int(window_left), int(window_right),
                                 _dtype_code(q), int(chunk_keys), _ptr(workspace),
@@ -224,24 +269,53 @@ def _need_int32(*ts):
             raise TypeError("offset, length and index tensors must be int32")
 
 
+def _need_workspace(ws, need):
+    if ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise TypeError("workspace must be a 1-D uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} needed")
+    _need_device(ws)
+
+
+def _need_cache(k_cache, v_cache, dims, strides, d, name="cache"):
+    """K and V caches of the same shape and dtype whose (block, token, head)
+    strides keep every element of `dims` = (num_blocks, block_size, Hkv)
+    heads of d values inside the tensor."""
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache must have the same shape")
+    if k_cache.dtype != v_cache.dtype:
+        raise TypeError("k_cache and v_cache must share a dtype")
+    nb, bs, hkv = dims
+    if min(nb, bs, hkv) < 1:
+        raise ValueError(f"{name} dimensions must be positive, got {dims}")
+    if min(int(x) for x in strides) < 0:
+        raise ValueError("cache strides must be non-negative")
+    last = (nb - 1) * int(strides[0]) + (bs - 1) * int(strides[1]) + (hkv - 1) * int(strides[2]) + d
+    if last > k_cache.numel():
+        raise ValueError(f"{name} strides {tuple(strides)} reach element {last}, "
+                         f"past the {k_cache.numel()} elements of the cache")
+
+
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale, window_left=-1,
                     window_right=-1, out=None, lse=None, stream=None):
     """Ragged batch in packed layout: q [total_q, H, d]; k, v [total_k, Hkv, d];
     cu_seqlens_q/k int32 [num_seqs + 1] on the device.  Returns O [total_q, H, d]
     and LSE [H, total_q].  (-1, 0) windows give the causal mask."""
     lib = load_library()
-    _need_device(q, k, v, cu_seqlens_q, cu_seqlens_k)
     _need_int32(cu_seqlens_q, cu_seqlens_k)
+    _need_dims(q, 3, "q")
+    _need_dims(k, 3, "k")
     total_q, H, d = q.shape
     total_k, Hkv = k.shape[0], k.shape[1]
     if k.shape != (total_k, Hkv, d) or v.shape != k.shape:
         raise ValueError("k and v must be [total_k, Hkv, d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
     num_seqs = cu_seqlens_q.numel() - 1
     if cu_seqlens_k.numel() != num_seqs + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have num_seqs + 1 entries")
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need_device(out, lse)
+    out, lse = _out_lse(out, lse, (total_q, H, d), (H, total_q), q.dtype, q.device)
+    _need_device(q, k, v, cu_seqlens_q, cu_seqlens_k, out, lse)
     _check(lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), num_seqs, total_q, total_k,
                                int(max_seqlen_q), H, Hkv, d, float(scale), int(window_left),
@@ -259,19 +333,24 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k
     [num_seqs + 1]; seqlens_k int32 [num_seqs].  Each sequence's queries are
     the last positions of its cached context.  Returns O and LSE [Hq, total_q]."""
     lib = load_library()
-    _need_device(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k)
     _need_int32(block_table, cu_seqlens_q, seqlens_k)
+    _need_dims(q, 3, "q")
+    _need_dims(block_table, 2, "block_table")
     total_q, Hq, d = q.shape
-    nb, block_size, Hkv = _cache_dims(k_cache, cache_dims)
+    nb, block_size, Hkv = _cache_dims(k_cache, cache_dims, d, strides is not None)
     num_blocks = nb if num_blocks is None else num_blocks
+    if num_blocks > nb:
+        raise ValueError(f"num_blocks {num_blocks} exceeds the cache's {nb} blocks")
     num_seqs = cu_seqlens_q.numel() - 1
     if seqlens_k.numel() != num_seqs or block_table.shape[0] != num_seqs:
         raise ValueError("seqlens_k and block_table must have num_seqs rows")
     if strides is None:
         strides = (block_size * Hkv * d, Hkv * d, d)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need_device(out, lse)
+    _need_cache(k_cache, v_cache, (nb, block_size, Hkv), strides, d)
+    if k_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share a dtype")
+    out, lse = _out_lse(out, lse, (total_q, Hq, d), (Hq, total_q), q.dtype, q.device)
+    _need_device(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, out, lse)
     _check(lib.attn_prefill_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cu_seqlens_q),
         _ptr(seqlens_k), _ptr(out), _ptr(lse), num_seqs, total_q, int(max_seqlen_q), Hq, Hkv, d,
@@ -305,11 +384,17 @@ def attn_decode_paged_workspace_size(num_seqs, Hq, d, max_context, chunk_tokens=
                                                                chunk_tokens))
 
 
-def _cache_dims(k_cache, cache_dims):
-    """(num_blocks, block_size, Hkv): from a [blocks, slots, heads, d] shape, or
-    given explicitly for other layouts (e.g. head-major pages via strides)."""
+def _cache_dims(k_cache, cache_dims, d, strided):
+    """(num_blocks, block_size, Hkv): from a [blocks, slots, heads, d] shape
+    (rows of more than d values only with explicit strides), or given
+    explicitly for other layouts (e.g. head-major pages via strides)."""
     if cache_dims is not None:
+        if len(cache_dims) != 3:
+            raise ValueError("cache_dims must be (num_blocks, block_size, Hkv)")
         return tuple(int(x) for x in cache_dims)
+    _need_dims(k_cache, 4, "k_cache")
+    if k_cache.shape[3] < d or (not strided and k_cache.shape[3] != d):
+        raise ValueError(f"k_cache rows hold {k_cache.shape[3]} values, q has d = {d}")
     return k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
 
 
@@ -328,21 +413,27 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, scale, max
     head) pairs, laid end to end, into equal ranges.
     """
     lib = load_library()
-    _need_device(q, k_cache, v_cache, block_table, context_lens)
+    _need_int32(block_table, context_lens)
+    _need_dims(q, 3, "q")
+    _need_dims(block_table, 2, "block_table")
     num_seqs, Hq, d = q.shape
-    num_blocks, block_size, Hkv = _cache_dims(k_cache, cache_dims)
-    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise TypeError("block_table and context_lens must be int32")
+    num_blocks, block_size, Hkv = _cache_dims(k_cache, cache_dims, d, strides is not None)
+    if block_table.shape[0] != num_seqs:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows for {num_seqs} sequences")
+    if context_lens.numel() != num_seqs:
+        raise ValueError(f"context_lens has {context_lens.numel()} entries for {num_seqs} sequences")
     max_blocks = block_table.shape[1]
     if strides is None:
         strides = (block_size * Hkv * d, Hkv * d, d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((num_seqs, Hq), dtype=torch.float32, device=q.device)
+    _need_cache(k_cache, v_cache, (num_blocks, block_size, Hkv), strides, d)
+    if k_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share a dtype")
+    out, lse = _out_lse(out, lse, (num_seqs, Hq, d), (num_seqs, Hq), q.dtype, q.device)
     need = attn_decode_paged_workspace_size(num_seqs, Hq, d, max_context, chunk_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need_workspace(workspace, need)
+    _need_device(q, k_cache, v_cache, block_table, context_lens, out, lse)
     _check(lib.attn_decode_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(context_lens),
         _ptr(out), _ptr(lse), num_seqs, Hq, Hkv, d, block_size, num_blocks, max_blocks,
@@ -356,15 +447,29 @@ def attn_bwd_workspace_size(B, H, Nq, d):
 
 
 def _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace):
-    _need_device(q, k, v, o, do, lse)
+    _need_dims(q, 4, "q")
+    _need_dims(k, 4, "k")
     B, H, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, Nk, d]")
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _need_dtype(t, q.dtype, name)
+    _need_shape(o, q.shape, "o")
+    _need_shape(do, q.shape, "do")
+    _need_shape(lse, (B, H, Nq), "lse")
+    _need_dtype(lse, torch.float32, "lse")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _need_shape(t, ref.shape, name)
+        _need_dtype(t, q.dtype, name)
     need = attn_bwd_workspace_size(B, H, Nq, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need_workspace(workspace, need)
+    _need_device(q, k, v, o, do, lse, dq, dk, dv)
     return (B, H, Hkv, Nq, Nk, d), dq, dk, dv, workspace
 
 

@@ -479,13 +479,16 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_con
   return most;
 }
 
-attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache,
-                                const int32_t* block_table, const int32_t* context_lens, void* O,
-                                float* LSE, int num_seqs, int Hq, int Hkv, int d, int block_size,
-                                int num_blocks, int max_blocks_per_seq, int max_context,
-                                int64_t block_stride, int64_t token_stride, int64_t head_stride,
-                                float scale, attn_dtype_t dtype, int chunk_tokens,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Validation and launch of a paged decode into the caller's workspace.
+attn_status_t decode_impl(const void* Q, const void* K_cache, const void* V_cache,
+                          const int32_t* block_table, const int32_t* context_lens, void* O,
+                          float* LSE, int num_seqs, int Hq, int Hkv, int d, int block_size,
+                          int num_blocks, int max_blocks_per_seq, int max_context,
+                          int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                          float scale, attn_dtype_t dtype, int chunk_tokens, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   if (!Q || !K_cache || !V_cache || !block_table || !context_lens || !O)
     return fail(ATTN_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(Q) || !aligned16(K_cache) || !aligned16(V_cache) || !aligned16(O) ||
@@ -533,6 +536,21 @@ attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* 
   hipError_t e = eta::launch_decode(a, p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* V_cache,
+                                const int32_t* block_table, const int32_t* context_lens, void* O,
+                                float* LSE, int num_seqs, int Hq, int Hkv, int d, int block_size,
+                                int num_blocks, int max_blocks_per_seq, int max_context,
+                                int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                                float scale, attn_dtype_t dtype, int chunk_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(Q, K_cache, V_cache, block_table, context_lens, O, LSE, num_seqs, Hq, Hkv,
+                     d, block_size, num_blocks, max_blocks_per_seq, max_context, block_stride,
+                     token_stride, head_stride, scale, dtype, chunk_tokens, workspace,
+                     workspace_bytes, stream);
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int Nq, int d) {

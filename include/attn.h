@@ -109,7 +109,11 @@ attn_status_t attn_fwd_local(const void* Q, const void* K, const void* V, void* 
 /*
  * Bytes of workspace attn_fwd_splitkv needs (0 when it will not split the
  * key range for these sizes, or when the arguments are invalid).  Window
- * sides and chunk_keys as for attn_fwd_splitkv.
+ * sides and chunk_keys as for attn_fwd_splitkv.  The workspace holds, per
+ * query row and key part, the unnormalised partial result: the accumulator o
+ * (fp32, d values), its reference maximum and its sum ("Attention kernels",
+ * FlashDecoding paragraph: partials of separate key ranges, combined exactly
+ * by rescaling with their maxima and sums).  Host function; no device work.
  */
 size_t attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int window_left,
                                        int window_right, int chunk_keys);
@@ -221,7 +225,11 @@ attn_status_t attn_fwd_block_sparse(const void* Q, const void* K, const void* V,
 /*
  * Bytes of workspace attn_decode_paged needs for these sizes and any number
  * of KV heads (0 when the arguments are invalid).  chunk_tokens as for
- * attn_decode_paged.
+ * attn_decode_paged.  The workspace holds the split-context partials of
+ * "Attention kernels", FlashDecoding paragraph: per piece of a context, the
+ * unnormalised o (fp32, per query head of the group), its maximum and sum,
+ * plus each (sequence, KV head) pair's first and last piece index for the
+ * merge.  Host function; no device work.
  */
 size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_context,
                                         int chunk_tokens);
@@ -280,8 +288,13 @@ attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* 
                                 float scale, attn_dtype_t dtype, int chunk_tokens,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace attn_bwd needs: two fp32 values per query row (the row
- * term D = rowsum(dO * O) and the base-2 log-sum-exp). */
+/*
+ * Bytes of workspace attn_bwd needs: two fp32 values per query row, the row
+ * term D = rowsum(dO * O) and the base-2 log-sum-exp.  These are the compact
+ * per-row statistics the backward keeps instead of P ("Modern attention
+ * kernels", "Backward pass recomputes scores"; "Flash attention and
+ * IO-aware attention", backward paragraph).  Host function; no device work.
+ */
 size_t attn_bwd_workspace_size(int B, int H, int Nq, int d);
 
 /*
@@ -325,10 +338,22 @@ attn_status_t attn_bwd_local(const void* Q, const void* K, const void* V, const 
 int attn_plan_describe(int phase, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
                        attn_dtype_t dtype, char* buf, size_t len);
 
-/* Static string naming a status code. */
+/*
+ * Static string naming a status code (never NULL; a code outside the enum
+ * gives "ATTN_ERR_UNKNOWN").  The codes report inputs the kernels would otherwise
+ * mishandle, checked on the host before any launch: shapes a path does not
+ * support, strides and block layouts that disagree with the cache
+ * ("Modern attention kernels", "Failure modes": page-table mismatch between
+ * allocator and kernel), workspaces that are too small.
+ */
 const char* attn_status_string(attn_status_t status);
 
-/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+/*
+ * Detail of the last non-OK status returned on the calling thread ("" if
+ * none): which argument failed which check (same passage as
+ * attn_status_string).  The string is owned by the library and valid until
+ * the thread's next call.
+ */
 const char* attn_last_error(void);
 
 #ifdef __cplusplus

@@ -66,6 +66,14 @@ def _check_shapes(q, k, v):
     return h // hkv
 
 
+def kv_head(h, n_heads, n_kv):
+    """KV head read by query head h, with n_heads query heads over n_kv KV
+    heads.  [AK]'s grouped-query paragraph has several query heads share one
+    KV head without saying which; the groups are taken contiguous: heads
+    h = g * G .. g * G + G - 1 read KV head g, G = n_heads / n_kv."""
+    return h // (n_heads // n_kv)
+
+
 def forward_probs(q, k, v, scale, causal, window=None, mask=None):
     """Materialised attention: returns (O, LSE, P).
 
@@ -99,7 +107,7 @@ def forward_probs(q, k, v, scale, causal, window=None, mask=None):
     probs = np.zeros((bsz, nh, nq, nk))
     for b in range(bsz):
         for h in range(nh):
-            g = h // group
+            g = kv_head(h, nh, nh // group)
             s = scale * (q[b, h] @ k[b, g].T)
             s = np.where(vis_all[b, h], s, -np.inf)
             m = s.max(axis=1) if nk > 0 else np.full(nq, -np.inf)
@@ -157,7 +165,7 @@ def backward(q, k, v, do, scale, causal, window=None):
     dv = np.zeros_like(v)
     for b in range(bsz):
         for h in range(nh):
-            g = h // group
+            g = kv_head(h, nh, nh // group)
             p = p_all[b, h]
             dv[b, g] += p.T @ do[b, h]
             dp = do[b, h] @ v[b, g].T

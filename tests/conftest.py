@@ -1,3 +1,4 @@
+import json
 import os
 import sys
 
@@ -12,10 +13,18 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
 
 
-def pytest_collection_modifyitems(config, items):
-    # GPU tests fail loudly when no GPU is present rather than silently
-    # passing, but only when they were actually selected (-m gpu).
-    pass
+def pytest_sessionfinish(session, exitstatus):
+    # Error figures of every parity comparison of the session (max-abs,
+    # mean-abs, max-rel), written as JSON when ETA_PARITY_LOG names a file.
+    path = os.environ.get("ETA_PARITY_LOG")
+    if not path:
+        return
+    import parity
+    d = os.path.dirname(path)
+    if d:
+        os.makedirs(d, exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(parity.LOG, f, indent=0)
 
 
 @pytest.fixture(scope="session")

@@ -2,7 +2,6 @@
 
 import math
 
-import numpy as np
 import pytest
 import torch
 
@@ -77,24 +76,18 @@ def test_bwd_very_negative_scores_ragged_keys(gpu):
 
 
 def test_causal_bwd_b2_h16_n4096_d128(gpu):
-    """B=2, H=16, N=4096, d=128, causal, scale 1/sqrt(128): full-size launch.
-    Two whole heads against the oracle; on every head the invariants
-    sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 (rows of P sum to one, rows of
-    dS sum to zero)."""
+    """B=2, H=16, N=4096, d=128, causal, scale 1/sqrt(128): full-size launch,
+    exactly as the benchmark calls it.  dQ, dK and dV of every (batch, head)
+    are compared with the oracle's gradients, one head at a time."""
     B, H, N, d = 2, 16, 4096, 128
     scale = 1.0 / math.sqrt(d)
     q, k, v, do = workloads.backward(B, H, H, N, N, d, dtype="bf16", seed=0)
     dq, dk, dv = _fwd_bwd(gpu, q, k, v, do, scale, True)
-    for b, h in [(0, 0), (1, H - 1)]:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        rq, rk, rv = oracle.backward(to64(q[sl]), to64(k[sl]), to64(v[sl]), to64(do[sl]),
-                                     scale, True)
-        check_grad(to64(dq[sl]), rq, f"dQ[{b},{h}]")
-        check_grad(to64(dk[sl]), rk, f"dK[{b},{h}]")
-        check_grad(to64(dv[sl]), rv, f"dV[{b},{h}]")
-    sdv = to64(dv).sum(axis=2)
-    sdo = to64(do).sum(axis=2)
-    # bf16 outputs: each of the N summed terms carries ~2^-9 relative rounding.
-    assert np.abs(sdv - sdo).max() <= 0.5, np.abs(sdv - sdo).max()
-    assert np.abs(to64(dk).sum(axis=2)).max() <= 0.5
-    assert torch.isfinite(dq.float()).all()
+    for b in range(B):
+        for h in range(H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            rq, rk, rv = oracle.backward(to64(q[sl]), to64(k[sl]), to64(v[sl]), to64(do[sl]),
+                                         scale, True)
+            check_grad(to64(dq[sl]), rq, f"dQ[{b},{h}]")
+            check_grad(to64(dk[sl]), rk, f"dK[{b},{h}]")
+            check_grad(to64(dv[sl]), rv, f"dV[{b},{h}]")

@@ -258,16 +258,19 @@ def test_decode_matches_last_row_of_causal_prefill(gpu):
     qpre[0, :, -1] = w["q"][0]
     o_pre, l_pre = attn.attn_fwd(qpre.to(gpu), kpre, vpre, 1 / math.sqrt(d), True)
     o_dec, l_dec = _decode(w, gpu, 1 / math.sqrt(d))
-    err = (o_pre[0, :, -1].float().cpu() - o_dec[0].float()).abs().max().item()
-    assert err <= 2e-2
-    assert (l_pre[0, :, -1].cpu() - l_dec[0]).abs().max().item() <= 1e-3
+    o_ref, lse_ref = _oracle(w, 1 / math.sqrt(d))
+    check_out(to64(o_dec), o_ref, "bf16", what="O decode vs oracle")
+    check_lse(to64(l_dec), lse_ref, "bf16", what="LSE decode vs oracle")
+    check_out(to64(o_pre[0, :, -1])[None], o_ref, "bf16", what="O prefill last row vs oracle")
+    check_lse(to64(l_pre[0, :, -1])[None], lse_ref, "bf16", what="LSE prefill last row vs oracle")
+    check_out(to64(o_pre[0, :, -1]), to64(o_dec[0]), "bf16", what="O prefill vs decode kernel")
 
 
-def test_paged_gqa_decode_64seq_full_size_sampled(gpu):
+def test_paged_gqa_decode_64seq_full_size(gpu):
     """64 sequences, Hq=32, Hkv=8, d=128, contexts uniform in [4096, 32768],
-    16-token pages from a seeded permutation; full-size launch with the
-    benchmark's automatic chunking, oracle on sampled sequences, and the
-    finite/LSE invariants on all of them."""
+    16-token pages from a seeded permutation, tail slots poisoned with NaN;
+    full-size launch with the benchmark's automatic split.  Every query head
+    of every sequence is compared with the oracle over its gathered context."""
     spec = workloads.WORKLOADS["paged_gqa_decode_bf16_s64_hq32_hkv8_d128"]
     w = workloads.decode(num_seqs=spec["num_seqs"], Hq=spec["Hq"], Hkv=spec["Hkv"], d=spec["d"],
                          ctx_lo=spec["ctx_lo"], ctx_hi=spec["ctx_hi"],
@@ -280,18 +283,18 @@ def test_paged_gqa_decode_64seq_full_size_sampled(gpu):
                                     g["context_lens"], scale, spec["ctx_hi"])
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
     bt = w["block_table"]
-    for s in [0, 17, 42, 63]:
+    bs = spec["block_size"]
+    for s in range(spec["num_seqs"]):
         ctx = int(w["context_lens"][s])
-        pages = bt[s, : (ctx + 15) // 16].long().to(gpu)
+        pages = bt[s, : (ctx + bs - 1) // bs].long().to(gpu)
         kk = w["k_cache"][pages].reshape(-1, spec["Hkv"], spec["d"])[:ctx].cpu()
         vv = w["v_cache"][pages].reshape(-1, spec["Hkv"], spec["d"])[:ctx].cpu()
         o_ref, lse_ref = oracle.forward(to64(w["q"][s].cpu())[None, :, None, :],
                                         to64(kk).transpose(1, 0, 2)[None],
                                         to64(vv).transpose(1, 0, 2)[None], scale, False)
-        check_out(to64(o[s]), o_ref[0, :, 0], "bf16", what=f"seq {s}")
-        check_lse(to64(lse[s]), lse_ref[0, :, 0], "bf16")
+        check_out(to64(o[s]), o_ref[0, :, 0], "bf16", what=f"O seq {s}")
+        check_lse(to64(lse[s]), lse_ref[0, :, 0], "bf16", what=f"LSE seq {s}")
 
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -91,29 +91,26 @@ def test_deterministic(gpu):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def _sampled_rows(q, k, v, o, lse, scale, causal, heads, rows):
-    """Oracle rows one by one: row i sees keys 0..i (+ Nk - Nq) under causal."""
-    nq, nk = q.shape[2], k.shape[2]
+def _compare_heads(q, k, v, o, lse, scale, causal):
+    """Every row of every (batch, head) against the oracle, one head at a time
+    (the oracle materialises one head's N x N scores and probabilities)."""
     group = q.shape[1] // k.shape[1]
-    for b, h in heads:
-        g = h // group
-        for i in rows:
-            vis = min(nk, i + (nk - nq) + 1) if causal else nk
-            qi = to64(q[b, h, i])[None, None, None]
-            ki = to64(k[b, g, :vis])[None, None]
-            vi = to64(v[b, g, :vis])[None, None]
-            o_ref, lse_ref = oracle.forward(qi, ki, vi, scale, False)
-            check_out(to64(o[b, h, i])[None], o_ref[0, 0], "bf16", what=f"O[{b},{h},{i}]")
-            check_lse(np.array([float(lse[b, h, i])]), lse_ref[0, 0], "bf16")
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            g = h // group
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            o_ref, lse_ref = oracle.forward(to64(q[sl]), to64(k[b:b + 1, g:g + 1]),
+                                            to64(v[b:b + 1, g:g + 1]), scale, causal)
+            check_out(to64(o[sl]), o_ref, "bf16", what=f"O[{b},{h}]")
+            check_lse(to64(lse[sl]), lse_ref, "bf16", what=f"LSE[{b},{h}]")
 
 
 @pytest.mark.parametrize("H,causal", [(32, True), (32, False), (4, True)])
-def test_long_prefill_n8192_d128_sampled(gpu, H, causal):
+def test_long_prefill_n8192_d128_full(gpu, H, causal):
     """B=1, N=8192, d=128, scale 1/sqrt(128): H=32 causal and non-causal, and
-    H=4 causal (small grid, finer sequence split).  Full-size launch; the
-    oracle checks sampled rows (tile edges, first/last rows) of several heads,
-    and every row's LSE is checked against an invariant that holds at any
-    size: LSE_i >= max visible score."""
+    H=4 causal (a small grid: the binding takes the key-split path).
+    Full-size launch, exactly as the benchmark calls it; every row of every
+    head is compared with the oracle (O to the bf16 bounds, LSE to 1e-3)."""
     N, d = 8192, 128
     scale = 1.0 / math.sqrt(d)
     q, k, v = workloads.prefill(1, H, H, N, N, d, dtype="bf16", seed=0)
@@ -121,10 +118,7 @@ def test_long_prefill_n8192_d128_sampled(gpu, H, causal):
     o, lse = attn.attn_fwd(qg, kg, vg, scale, causal)
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    rows = [0, 1, 31, 32, 63, 64, 127, 128, 129, 4095, 4096, 8127, 8128, 8190, 8191]
-    heads = [(0, 0), (0, H // 2), (0, H - 1)]
-    _sampled_rows(q, k, v, o, lse, scale, causal, heads, rows)
-    # Row 0 under causal sees only key 0: O = V[0] exactly up to bf16 rounding.
+    _compare_heads(q, k, v, o, lse, scale, causal)
+    # Row 0 under causal sees only key 0: O = V[0] exactly (bf16 in, bf16 out).
     if causal:
         assert torch.equal(o[0, :, 0], v[0, :, 0])

@@ -124,8 +124,13 @@ def test_prefill_paged_one_row_matches_decode_kernel(gpu):
                                     w["block_table"].to(gpu), w["seqlens_k"].to(gpu), scale,
                                     max(k_lens))
     torch.cuda.synchronize()
-    check_out(to64(o), to64(od), "bf16")
-    check_lse(to64(lse).T, to64(ld), "bf16")
+    o_ref, lse_ref = _paged_ref(w, scale, (-1, 0))
+    check_out(to64(o), o_ref, "bf16", what="O prefill kernel vs oracle")
+    check_lse(to64(lse), lse_ref, "bf16", what="LSE prefill kernel vs oracle")
+    check_out(to64(od), o_ref, "bf16", what="O decode kernel vs oracle")
+    check_lse(to64(ld).T, lse_ref, "bf16", what="LSE decode kernel vs oracle")
+    check_out(to64(o), to64(od), "bf16", what="O prefill vs decode kernel")
+    check_lse(to64(lse).T, to64(ld), "bf16", what="LSE prefill vs decode kernel")
 
 
 def test_prefill_paged_invalid_entries_are_skipped(gpu):
@@ -167,14 +172,20 @@ def test_prefill_paged_chunks_compose_full_prefill(gpu):
               max_q=n - split)
     o1, l1 = _paged(w1, gpu, scale, (-1, 0))
     o2, l2 = _paged(w2, gpu, scale, (-1, 0))
-    check_out(to64(torch.cat([o1, o2])), to64(o_full), "bf16")
-    check_lse(to64(torch.cat([l1, l2], dim=1)), to64(lse_full), "bf16")
+    o_ref, lse_ref = _paged_ref(w, scale, (-1, 0))
+    check_out(to64(o_full), o_ref, "bf16", what="O one shot vs oracle")
+    check_lse(to64(lse_full), lse_ref, "bf16", what="LSE one shot vs oracle")
+    check_out(to64(torch.cat([o1, o2])), o_ref, "bf16", what="O two chunks vs oracle")
+    check_lse(to64(torch.cat([l1, l2], dim=1)), lse_ref, "bf16", what="LSE two chunks vs oracle")
+    check_out(to64(torch.cat([o1, o2])), to64(o_full), "bf16", what="O two chunks vs one shot")
 
 
-def test_prefill_paged_serving_shape_sampled(gpu):
+def test_prefill_paged_serving_shape(gpu):
     """The benchmark's serving-shaped workload (16 sequences, GQA 32/8,
-    d = 128, 16-token pages) in the benchmark's launch configuration:
-    sampled sequences and query rows against the oracle."""
+    d = 128, 16-token pages) in the benchmark's launch configuration: every
+    query row of every sequence against the oracle, for the first query head
+    of the first KV group and the last query head of the last (the oracle
+    materialises each sequence's scores one head at a time)."""
     pw = workloads.WORKLOADS["paged_prefill_causal_bf16_s16_hq32_hkv8_d128"]
     num_seqs = pw["num_seqs"]
     w = workloads.serving_prefill(num_seqs, pw["q_lo"], pw["q_hi"], pw["ctx_lo"], pw["ctx_hi"],
@@ -183,45 +194,51 @@ def test_prefill_paged_serving_shape_sampled(gpu):
     q_lens, k_lens = w["q_lens"], w["k_lens"]
     scale = pw["scale"]
     o, lse = _paged(w, gpu, scale, (-1, 0))
+    o, lse = o.cpu(), lse.cpu()
     cu = w["cu_q"].tolist()
-    rng = np.random.default_rng(0)
+    group = pw["Hq"] // pw["Hkv"]
     kc, vc, bt = w["k_cache"].cpu().float().numpy(), w["v_cache"].cpu().float().numpy(), w["block_table"].numpy()
-    for s in rng.choice(num_seqs, 3, replace=False):
-        rows = np.sort(rng.choice(q_lens[s], 8, replace=False))
+    qh = w["q"].cpu()
+    for s in range(num_seqs):
         kk = oracle.gather_paged(kc, bt, s, k_lens[s]).astype(np.float64)
         vv = oracle.gather_paged(vc, bt, s, k_lens[s]).astype(np.float64)
-        # Row i of the chunk sits at position i + k - q and sees keys 0 .. that position.
-        pos = rows + k_lens[s] - q_lens[s]
-        vis = (np.arange(k_lens[s])[None, :] <= pos[:, None])[None, None]
-        qs = to64(w["q"][torch.as_tensor(cu[s] + rows)]).transpose(1, 0, 2)[None]
-        o_ref, lse_ref = oracle.forward(qs, kk.transpose(1, 0, 2)[None], vv.transpose(1, 0, 2)[None],
-                                        scale, False, mask=vis)
-        check_out(to64(o[torch.as_tensor(cu[s] + rows)]).transpose(1, 0, 2), o_ref[0], "bf16")
-        check_lse(to64(lse[:, torch.as_tensor(cu[s] + rows)]), lse_ref[0], "bf16")
+        for h in (0, pw["Hq"] - 1):
+            g = h // group
+            # The chunk's rows are the last q positions of the context: bottom-right causal.
+            qs = to64(qh[cu[s]:cu[s + 1], h])[None, None]
+            o_ref, lse_ref = oracle.forward(qs, kk[:, g][None, None], vv[:, g][None, None],
+                                            scale, True)
+            check_out(to64(o[cu[s]:cu[s + 1], h]), o_ref[0, 0], "bf16", what=f"O seq {s} head {h}")
+            check_lse(to64(lse[h, cu[s]:cu[s + 1]]), lse_ref[0, 0], "bf16",
+                      what=f"LSE seq {s} head {h}")
 
 
-def test_varlen_bench_shape_sampled(gpu):
+def test_varlen_bench_shape(gpu):
     """The benchmark's packed ragged workload (16 sequences of 512..8192
     tokens, GQA 32/8, d = 128, causal) in the benchmark's launch
-    configuration: sampled sequences and rows against the oracle."""
+    configuration: every row of every sequence against the oracle, for the
+    first query head of the first KV group and the last query head of the
+    last."""
     vw = workloads.WORKLOADS["varlen_causal_bf16_s16_h32_hkv8_d128"]
     lens = workloads.ragged_lengths(vw["num_seqs"], vw["len_lo"], vw["len_hi"], seed=vw["seed"] + 1)
     w = workloads.ragged(lens, lens, vw["H"], vw["Hkv"], vw["d"], seed=vw["seed"], device=str(gpu))
     o, lse = attn.attn_fwd_varlen(w["q"], w["k"], w["v"], w["cu_q"].to(gpu), w["cu_k"].to(gpu),
                                   w["max_q"], vw["scale"], -1, 0)
     torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    qh, kh, vh = w["q"].cpu(), w["k"].cpu(), w["v"].cpu()
     cu = w["cu_q"].tolist()
-    rng = np.random.default_rng(2)
-    for s in rng.choice(vw["num_seqs"], 3, replace=False):
-        n = lens[s]
-        rows = np.sort(rng.choice(n, 8, replace=False))
-        kk = to64(w["k"][cu[s]:cu[s + 1]]).transpose(1, 0, 2)[None]
-        vv = to64(w["v"][cu[s]:cu[s + 1]]).transpose(1, 0, 2)[None]
-        vis = (np.arange(n)[None, :] <= rows[:, None])[None, None]
-        qs = to64(w["q"][torch.as_tensor(cu[s] + rows)]).transpose(1, 0, 2)[None]
-        o_ref, lse_ref = oracle.forward(qs, kk, vv, vw["scale"], False, mask=vis)
-        check_out(to64(o[torch.as_tensor(cu[s] + rows)]).transpose(1, 0, 2), o_ref[0], "bf16")
-        check_lse(to64(lse[:, torch.as_tensor(cu[s] + rows)]), lse_ref[0], "bf16")
+    group = vw["H"] // vw["Hkv"]
+    for s in range(vw["num_seqs"]):
+        for h in (0, vw["H"] - 1):
+            g = h // group
+            qs = to64(qh[cu[s]:cu[s + 1], h])[None, None]
+            kk = to64(kh[cu[s]:cu[s + 1], g])[None, None]
+            vv = to64(vh[cu[s]:cu[s + 1], g])[None, None]
+            o_ref, lse_ref = oracle.forward(qs, kk, vv, vw["scale"], True)
+            check_out(to64(o[cu[s]:cu[s + 1], h]), o_ref[0, 0], "bf16", what=f"O seq {s} head {h}")
+            check_lse(to64(lse[h, cu[s]:cu[s + 1]]), lse_ref[0, 0], "bf16",
+                      what=f"LSE seq {s} head {h}")
 
 
 def test_prefill_paged_head_major_layout(gpu):
