@@ -45,6 +45,8 @@ EXPORTED = (
     "attn_bwd_local",
     "attn_decode_paged_workspace_size",
     "attn_decode_paged",
+    "attn_decode_paged_noalloc_max_bytes",
+    "attn_decode_paged_noalloc",
     "attn_bwd_workspace_size",
     "attn_bwd",
     "attn_plan_describe",
@@ -99,6 +101,11 @@ def load_library(path=LIB_PATH):
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                       i32, i32, i64, i64, i64, f32, i32, i32, vp, sz, vp]
     lib.attn_decode_paged.restype = i32
+    lib.attn_decode_paged_noalloc_max_bytes.argtypes = []
+    lib.attn_decode_paged_noalloc_max_bytes.restype = sz
+    lib.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                              i32, i32, i32, i64, i64, i64, f32, i32, i32, vp]
+    lib.attn_decode_paged_noalloc.restype = i32
     lib.attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.attn_bwd_workspace_size.restype = sz
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
@@ -439,6 +446,47 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, scale, max
         _ptr(out), _ptr(lse), num_seqs, Hq, Hkv, d, block_size, num_blocks, max_blocks,
         int(max_context), int(strides[0]), int(strides[1]), int(strides[2]), float(scale),
         _dtype_code(q), int(chunk_tokens), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def attn_decode_paged_noalloc_max_bytes():
+    return int(load_library().attn_decode_paged_noalloc_max_bytes())
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, context_lens, scale, max_context,
+                              out, lse, chunk_tokens=0, strides=None, stream=None,
+                              cache_dims=None):
+    """attn_decode_paged without a workspace: the library's static scratch
+    holds the partials, so the call allocates nothing (``out`` [num_seqs, Hq,
+    d] and ``lse`` [num_seqs, Hq] float32 are the caller's).  Calls that
+    overlap on one GPU share that scratch and race."""
+    lib = load_library()
+    _need_int32(block_table, context_lens)
+    _need_dims(q, 3, "q")
+    _need_dims(block_table, 2, "block_table")
+    num_seqs, Hq, d = q.shape
+    num_blocks, block_size, Hkv = _cache_dims(k_cache, cache_dims, d, strides is not None)
+    if block_table.shape[0] != num_seqs:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows for {num_seqs} sequences")
+    if context_lens.numel() != num_seqs:
+        raise ValueError(f"context_lens has {context_lens.numel()} entries for {num_seqs} sequences")
+    if strides is None:
+        strides = (block_size * Hkv * d, Hkv * d, d)
+    _need_cache(k_cache, v_cache, (num_blocks, block_size, Hkv), strides, d)
+    if k_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share a dtype")
+    if out is None or lse is None:
+        raise ValueError("out and lse must be given (this entry point allocates nothing)")
+    _need_shape(out, (num_seqs, Hq, d), "out")
+    _need_dtype(out, q.dtype, "out")
+    _need_shape(lse, (num_seqs, Hq), "lse")
+    _need_dtype(lse, torch.float32, "lse")
+    _need_device(q, k_cache, v_cache, block_table, context_lens, out, lse)
+    _check(lib.attn_decode_paged_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(context_lens),
+        _ptr(out), _ptr(lse), num_seqs, Hq, Hkv, d, block_size, num_blocks,
+        block_table.shape[1], int(max_context), int(strides[0]), int(strides[1]),
+        int(strides[2]), float(scale), _dtype_code(q), int(chunk_tokens), _stream(stream)))
     return out, lse
 
 

@@ -11,6 +11,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "kernels.hpp"
 
@@ -36,6 +38,41 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 using eta::kNumCU;
 
 constexpr long long kMaxGrid = 0x7fffffffLL;
+
+}  // namespace
+
+// Scratch of attn_decode_paged_noalloc (the split partials and the pairs'
+// segment ids, the same contents as attn_decode_paged's workspace): a
+// file-scope device array, so that entry point never allocates.  Every GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code the name `scratch` is only a stand-in for the symbol: the device
+// address comes from hipGetSymbolAddress, once per device (decode_scratch).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev` (the current device), looked
+// up on the first call for that device and kept.
+attn_status_t decode_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ATTN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
 
 // ---------------------------------------------------------------- forward
 
@@ -481,14 +518,16 @@ size_t attn_decode_paged_workspace_size(int num_seqs, int Hq, int d, int max_con
 
 namespace {
 
-// Validation and launch of a paged decode into the caller's workspace.
+// Validation and launch shared by the two decode entry points.  `workspace`
+// is the caller's buffer, or (no_alloc) the library's static scratch, whose
+// capacity is workspace_bytes.
 attn_status_t decode_impl(const void* Q, const void* K_cache, const void* V_cache,
                           const int32_t* block_table, const int32_t* context_lens, void* O,
                           float* LSE, int num_seqs, int Hq, int Hkv, int d, int block_size,
                           int num_blocks, int max_blocks_per_seq, int max_context,
                           int64_t block_stride, int64_t token_stride, int64_t head_stride,
                           float scale, attn_dtype_t dtype, int chunk_tokens, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, void* stream, bool no_alloc) {
   if (!Q || !K_cache || !V_cache || !block_table || !context_lens || !O)
     return fail(ATTN_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(Q) || !aligned16(K_cache) || !aligned16(V_cache) || !aligned16(O) ||
@@ -523,10 +562,29 @@ attn_status_t decode_impl(const void* Q, const void* K_cache, const void* V_cach
     return fail(ATTN_ERR_UNSUPPORTED, "decode needs %lld split waves for %lld pairs",
                 n_waves, pairs);
   const size_t need = eta::decode_workspace_bytes(pairs, Hq / Hkv, d, n_waves);
-  if (!workspace || workspace_bytes < need)
-    return fail(ATTN_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (no_alloc) {
+    if (need > workspace_bytes)
+      return fail(ATTN_ERR_WORKSPACE,
+                  "decode needs %zu bytes of scratch, the no-allocation entry point holds %zu",
+                  need, workspace_bytes);
+    // The scratch pointer belongs to the current device: the stream must too.
+    int cur = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess)
+      return fail(ATTN_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+    if (sdev != cur)
+      return fail(ATTN_ERR_INVALID_ARG, "stream belongs to device %d, device %d is current",
+                  sdev, cur);
+    st = decode_scratch(cur, &workspace);
+    if (st != ATTN_OK) return st;
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(ATTN_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace))
+      return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
   eta::DecodeArgs a{Q,        K_cache,     V_cache,      block_table,  context_lens,
                     O,        LSE,         num_seqs,     Hq,           Hkv,
                     d,        block_size,  num_blocks,   max_blocks_per_seq,
@@ -550,7 +608,22 @@ attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* 
   return decode_impl(Q, K_cache, V_cache, block_table, context_lens, O, LSE, num_seqs, Hq, Hkv,
                      d, block_size, num_blocks, max_blocks_per_seq, max_context, block_stride,
                      token_stride, head_stride, scale, dtype, chunk_tokens, workspace,
-                     workspace_bytes, stream);
+                     workspace_bytes, stream, false);
+}
+
+size_t attn_decode_paged_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+attn_status_t attn_decode_paged_noalloc(const void* Q, const void* K_cache, const void* V_cache,
+                                        const int32_t* block_table, const int32_t* context_lens,
+                                        void* O, float* LSE, int num_seqs, int Hq, int Hkv, int d,
+                                        int block_size, int num_blocks, int max_blocks_per_seq,
+                                        int max_context, int64_t block_stride,
+                                        int64_t token_stride, int64_t head_stride, float scale,
+                                        attn_dtype_t dtype, int chunk_tokens, void* stream) {
+  return decode_impl(Q, K_cache, V_cache, block_table, context_lens, O, LSE, num_seqs, Hq, Hkv,
+                     d, block_size, num_blocks, max_blocks_per_seq, max_context, block_stride,
+                     token_stride, head_stride, scale, dtype, chunk_tokens, nullptr,
+                     kNoAllocScratchBytes, stream, true);
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int Nq, int d) {

@@ -289,6 +289,36 @@ attn_status_t attn_decode_paged(const void* Q, const void* K_cache, const void* 
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of the library's own scratch behind attn_decode_paged_noalloc (16 MiB):
+ * calls whose attn_decode_paged workspace, computed for their Hkv, would
+ * exceed it are rejected.  Host function; no device work.
+ */
+size_t attn_decode_paged_noalloc_max_bytes(void);
+
+/*
+ * attn_decode_paged for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as attn_decode_paged, minus
+ * the workspace: the split partials go to a static device array of
+ * attn_decode_paged_noalloc_max_bytes() bytes that each GPU holds from the
+ * first call on it until the process ends.  Nothing is allocated or freed.
+ *   Sizes whose partials do not fit give ATTN_ERR_WORKSPACE before any work.
+ *   `stream` must belong to the current device (else ATTN_ERR_INVALID_ARG).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (on different streams, or from different threads without ordering)
+ *   race and give undefined results; calls ordered on one stream are safe.
+ *   The array keeps the last call's contents; each call writes every entry it
+ *   reads before reading it, so nothing needs clearing between calls.
+ */
+attn_status_t attn_decode_paged_noalloc(const void* Q, const void* K_cache, const void* V_cache,
+                                        const int32_t* block_table, const int32_t* context_lens,
+                                        void* O, float* LSE, int num_seqs, int Hq, int Hkv, int d,
+                                        int block_size, int num_blocks, int max_blocks_per_seq,
+                                        int max_context, int64_t block_stride,
+                                        int64_t token_stride, int64_t head_stride, float scale,
+                                        attn_dtype_t dtype, int chunk_tokens, void* stream);
+
+/*
  * Bytes of workspace attn_bwd needs: two fp32 values per query row, the row
  * term D = rowsum(dO * O) and the base-2 log-sum-exp.  These are the compact
  * per-row statistics the backward keeps instead of P ("Modern attention

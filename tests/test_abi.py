@@ -109,6 +109,39 @@ def test_decode_validation(lib, cpu_only, kw, status):
     assert _decode(lib, **kw) == status
 
 
+def _decode_noalloc(lib, q=FAKE, num_seqs=2, Hq=8, Hkv=2, d=128, max_context=64, max_blocks=4,
+                    chunk=0):
+    strides = (16 * Hkv * d, Hkv * d, d)
+    return lib.attn_decode_paged_noalloc(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, num_seqs, Hq, Hkv,
+                                         d, 16, 10, max_blocks, max_context, strides[0],
+                                         strides[1], strides[2], 0.1, attn.ATTN_DTYPE_BF16, chunk,
+                                         NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), attn.ATTN_ERR_INVALID_ARG),
+    (dict(d=80), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(chunk=48), attn.ATTN_ERR_INVALID_ARG),
+    # 4096 sequences x 8 KV heads: partials of 33,792 segments x 4 heads x
+    # 130 floats, past the 16 MiB scratch.
+    (dict(num_seqs=4096, Hq=32, Hkv=8, max_blocks=2048, max_context=32768),
+     attn.ATTN_ERR_WORKSPACE),
+])
+def test_decode_noalloc_validation(lib, cpu_only, kw, status):
+    """The no-allocation decode validates like attn_decode_paged and refuses
+    sizes whose partials exceed its static scratch, before any device call."""
+    assert _decode_noalloc(lib, **kw) == status
+
+
+def test_decode_noalloc_capacity(lib):
+    cap = attn.attn_decode_paged_noalloc_max_bytes()
+    assert cap == 16 << 20
+    # The benchmark batch (64 sequences, Hq = 32, Hkv = 8, d = 128, contexts
+    # up to 32768 tokens) fits: 1024 split waves + 512 pairs, 4 heads each.
+    need = (1024 + 512) * 4 * (128 + 2) * 4 + 512 * 2 * 4
+    assert need <= cap
+
+
 def _bwd(lib, ws=FAKE, ws_bytes=1 << 30, dtype=attn.ATTN_DTYPE_BF16, d=128, dq=FAKE, H=4, Hkv=2):
     return lib.attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, 1, H, Hkv, 16, 16, d,
                         0.1, 1, dtype, ws, ws_bytes, NULL)
