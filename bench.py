@@ -47,6 +47,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector and MFMA)
 METRIC = "fwd attention TFLOP/s & % bf16 MFMA peak; paged decode KV GB/s % HBM peak"
 
 
@@ -218,6 +219,13 @@ def main():
     c2_flops = 4.0 * c2["B"] * c2["H"] * c2["Nq"] * c2["Nk"] * c2["d"] / 2.0
     nc = workloads.WORKLOADS["noncausal_bf16_b1_h32_n8192_d128"]
     nc_flops = 4.0 * nc["B"] * nc["H"] * nc["Nq"] * nc["Nk"] * nc["d"]
+    # The single-head fp32 configuration (B=1, H=1, N=512, d=64, non-causal).
+    c1 = workloads.WORKLOADS["single_head_f32_n512_d64"]
+    c1q, c1k, c1v = workloads.prefill(c1["B"], c1["H"], c1["Hkv"], c1["Nq"], c1["Nk"], c1["d"],
+                                      dtype="f32", seed=c1["seed"], device=str(dev))
+    c1o = torch.empty_like(c1q)
+    c1lse = torch.empty((c1["B"], c1["H"], c1["Nq"]), dtype=torch.float32, device=dev)
+    c1_flops = 4.0 * c1["B"] * c1["H"] * c1["Nq"] * c1["Nk"] * c1["d"]
 
     # Context for the MFMA roofline: the vendor's bf16 GEMM (torch.matmul)
     # on this GPU, timed the same way -- the sustained rate dense MFMA work
@@ -230,6 +238,8 @@ def main():
     # The vendor GEMM goes last: its sustained MFMA load lowers the clocks
     # the calls after it would get.
     extras = [
+        ("fwd_f32_config1", c1_flops, lambda: attn.attn_fwd(c1q, c1k, c1v, c1["scale"], False,
+                                                            out=c1o, lse=c1lse, stream=stream)),
         ("fwd_d64", c2_flops, lambda: attn.attn_fwd(c2q, c2k, c2v, c2["scale"], True, out=c2o,
                                                     lse=c2lse, stream=stream)),
         ("fwd_noncausal", nc_flops, lambda: attn.attn_fwd(q, k, v, nc["scale"], False, out=o,
@@ -378,6 +388,17 @@ def main():
                         "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                         "avg_call_ms": round(avg, 4), "flop_per_call": flops, "note": note}
 
+    avg, _, flops, _ = extra["fwd_f32_config1"]
+    result["config1_f32"] = {
+        "workload": "single_head_f32_n512_d64 (attn_fwd, fp32 inputs and accumulation)",
+        "ms": round(avg, 4), "value": round(flops / (avg * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "frac_fp32_peak": round(flops / (avg * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+        "flop_per_call": flops,
+        "note": "one 128-row query tile per 4-wave workgroup, 4 workgroups: latency-bound"}
+    # Clocks cannot be pinned without administrator rights; the GFX clock is
+    # sampled while the headline forward runs back to back instead.
+    result["clock"] = _gfx_clock_during(
+        lambda: attn.attn_fwd(q, k, v, fw["scale"], True, out=o, lse=lse, stream=stream))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, fw, args.cpu_heads)
     print(json.dumps(result))
@@ -516,6 +537,51 @@ def _sparse_pairs(row_ptr, col_idx, block=128):
     return pairs
 
 
+def _gfx_clock_during(call, seconds=0.3):
+    """GFX clock in MHz (amdsmi) sampled while `call` runs back to back:
+    batches of calls are queued and the clock is read while they run.
+    Returns the median, range and the driver's maximum, or the error."""
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+        read = lambda: amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)  # noqa: E731
+        first = read()
+    except Exception as exc:  # no SMI access: report why, keep the bench line
+        return {"error": f"{type(exc).__name__}: {exc}"}
+    samples = []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            call()
+        try:
+            samples.append(int(read()["clk"]))
+        except Exception:
+            pass
+        torch.cuda.synchronize()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    s = sorted(samples[len(samples) // 4:]) or [0]  # after the first quarter (settling)
+    return {"gfx_mhz_median_during_fwd": s[len(s) // 2], "gfx_mhz_min": s[0], "gfx_mhz_max": s[-1],
+            "samples": len(s), "driver_max_mhz": first.get("max_clk"),
+            "locked": first.get("clk_locked"), "pinned": False,
+            "note": "peaks are quoted at 2400 MHz; clocks cannot be pinned without root"}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(q, k, v, fw, heads):
     """The fp64 oracle, as it stands, timed on the host over a bounded sample:
     `heads` of the forward workload's heads, scaled to TFLOP/s with the same
@@ -539,6 +605,9 @@ def cpu_baseline(q, k, v, fw, heads):
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": cores,
+        "os_cpu_count": os.cpu_count(),
+        "cpu_model": _cpu_model(),
+        "blas_threads": cores,
         "kind": "oracle",
         "sample": f"{heads} of {fw['H']} heads of causal_bf16_b1_h32_n8192_d128 "
                   f"(fp64 numpy, materialised S and P), {dt:.1f} s",
