@@ -153,6 +153,7 @@ __device__ __forceinline__ void grid_tile(int wg, int n_qtiles, int B, int H, in
 // m + log2 l are the same for any reference point, so the result is exact as
 // with a per-tile rescale, while exponents stay <= 2^kSlack.
 constexpr float kSlack = 8.f;
+constexpr float kSlackExp = 256.f;  // 2^kSlack
 
 
 // Where a workgroup's rows live and which key tiles it visits.
@@ -479,48 +480,58 @@ void fwd_bf16_kernel(
           }
       }
 
-      // Online softmax update for this lane's row.
-      float mx = s[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-      for (int kb = 1; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      const float mx2 = halves_max(mx) * scale_log2;
-      if (wave_any(mx2 > m_run + kSlack)) {
-        const float m_new = fmaxf(m_run, mx2);
-        const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
-          s[kb][r] = p;
-          rs += p;
-        }
-      l_run += rs;
-
-      // P (bf16) as the B operand of o^T += V^T P^T, 16 keys per MFMA.
+      // Online softmax update for this lane's row, P packed to bf16 as the
+      // B operand of o^T += V^T P^T (16 keys per MFMA).  Common path: the
+      // exponentials against the current reference, without the tile's
+      // maximum.  When every lane's sum is at most 2^kSlack, no probability
+      // exceeded 2^kSlack, so the maximum could not have moved the reference
+      // and the result is exactly that of the full update below; otherwise
+      // (or before the row's first visible key) the full update runs from
+      // the scores, which are still intact.
       bf16x8 pb[KB][2];
+      float rs = 0.f;
+      auto exps = [&](float m_use) {
+        rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          u32x4 w;
+          for (int s2 = 0; s2 < 2; ++s2) {
+            u32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[kb][8 * s2 + 2 * e], s[kb][8 * s2 + 2 * e + 1]);
-          pb[kb][s2] = __builtin_bit_cast(bf16x8, w);
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * s2 + 2 * e;
+              const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
+              const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], scale_log2, -m_use));
+              rs += p0;
+              rs += p1;
+              w[e] = pack_bf16x2(p0, p1);
+            }
+            pb[kb][s2] = __builtin_bit_cast(bf16x8, w);
+          }
+      };
+      exps(m_run == -INFINITY ? 0.f : m_run);
+      if (wave_any(!(rs <= kSlackExp) || m_run == -INFINITY)) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+        for (int kb = 1; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        const float mx2 = halves_max(mx) * scale_log2;
+        if (wave_any(mx2 > m_run + kSlack)) {
+          const float m_new = fmaxf(m_run, mx2);
+          const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
         }
+        exps(m_run == -INFINITY ? 0.f : m_run);
+      }
+      l_run += rs;
       // o^T += V^T P^T: 4 MFMAs per 32-column block, V^T operands read one
       // MFMA ahead.
       constexpr int PV = 2 * KB;  // 16-key MFMA steps per tile

@@ -122,3 +122,40 @@ def test_long_prefill_n8192_d128_full(gpu, H, causal):
     # Row 0 under causal sees only key 0: O = V[0] exactly (bf16 in, bf16 out).
     if causal:
         assert torch.equal(o[0, :, 0], v[0, :, 0])
+
+
+# Wide grids (hundreds of heads) with ragged, rectangular, windowed and
+# grouped-query shapes: every workgroup slot of the chip in use at once.
+WIDE_CASES = [
+    # B, H, Hkv, Nq, Nk, window (left, right) or None for no mask
+    (1, 256, 256, 300, 300, (-1, 0)),
+    (1, 256, 64, 257, 257, None),
+    (2, 128, 32, 200, 900, (-1, 0)),     # Nq < Nk, bottom-right causal
+    (1, 256, 256, 900, 200, (-1, 0)),    # Nq > Nk: early rows see no key
+    (1, 256, 128, 513, 513, (63, 0)),    # sliding window of 64 keys
+    (1, 256, 256, 300, 300, (40, 17)),   # two-sided band
+    (1, 256, 256, 1, 64, (-1, 0)),       # one query row per head
+]
+
+
+@pytest.mark.parametrize("case", range(len(WIDE_CASES)))
+@pytest.mark.parametrize("d", [64, 128])
+def test_wide_grid_edges(gpu, case, d):
+    B, H, Hkv, Nq, Nk, window = WIDE_CASES[case]
+    q, k, v = workloads.prefill(B, H, Hkv, Nq, Nk, d, dtype="bf16", seed=case * 7 + d)
+    scale = 1.0 / math.sqrt(d)
+    qg, kg, vg = q.to(gpu), k.to(gpu), v.to(gpu)
+    if window is None:
+        o, lse = attn.attn_fwd(qg, kg, vg, scale, False)
+        band = None
+    elif window == (-1, 0):
+        o, lse = attn.attn_fwd(qg, kg, vg, scale, True)
+        band = None
+    else:
+        o, lse = attn.attn_fwd_local(qg, kg, vg, scale, *window)
+        band = (window[0], window[1])
+    torch.cuda.synchronize()
+    causal = window == (-1, 0)
+    o_ref, lse_ref = oracle.forward(to64(q), to64(k), to64(v), scale, causal, band)
+    check_out(to64(o), o_ref, "bf16")
+    check_lse(to64(lse), lse_ref, "bf16")
