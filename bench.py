@@ -537,26 +537,42 @@ def _sparse_pairs(row_ptr, col_idx, block=128):
     return pairs
 
 
-def _gfx_clock_during(call, seconds=0.3):
-    """GFX clock in MHz (amdsmi) sampled while `call` runs back to back:
-    batches of calls are queued and the clock is read while they run.
-    Returns the median, range and the driver's maximum, or the error."""
+def _gfx_clock_during(call, seconds=1.0):
+    """GFX clock and socket power (amdsmi clock and power queries) sampled
+    while `call` runs back to back: batches of calls are queued and both are
+    read while they run.  Returns the median and range over the samples
+    after the first quarter (settling), the board's power limit, or the
+    error.  (amdsmi's GPU-metrics table is not used: it held the same stale
+    idle values for the whole run.)"""
     import torch
     try:
         import amdsmi
         amdsmi.amdsmi_init()
         handle = amdsmi.amdsmi_get_processor_handles()[0]
-        read = lambda: amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)  # noqa: E731
-        first = read()
+        clk = lambda: amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)  # noqa: E731
+        pwr = lambda: amdsmi.amdsmi_get_power_info(handle)  # noqa: E731
+        first_clk, first_pwr = clk(), pwr()
     except Exception as exc:  # no SMI access: report why, keep the bench line
         return {"error": f"{type(exc).__name__}: {exc}"}
-    samples = []
+
+    def num(x):
+        try:
+            return float(x)
+        except (TypeError, ValueError):
+            return None
+
+    mhz, watts = [], []
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         for _ in range(8):
             call()
         try:
-            samples.append(int(read()["clk"]))
+            c = num(clk().get("clk"))
+            w = num(pwr().get("current_socket_power"))
+            if c:
+                mhz.append(c)
+            if w:
+                watts.append(w)
         except Exception:
             pass
         torch.cuda.synchronize()
@@ -564,11 +580,21 @@ def _gfx_clock_during(call, seconds=0.3):
         amdsmi.amdsmi_shut_down()
     except Exception:
         pass
-    s = sorted(samples[len(samples) // 4:]) or [0]  # after the first quarter (settling)
-    return {"gfx_mhz_median_during_fwd": s[len(s) // 2], "gfx_mhz_min": s[0], "gfx_mhz_max": s[-1],
-            "samples": len(s), "driver_max_mhz": first.get("max_clk"),
-            "locked": first.get("clk_locked"), "pinned": False,
-            "note": "peaks are quoted at 2400 MHz; clocks cannot be pinned without root"}
+
+    def stats(v):
+        v = sorted(v[len(v) // 4:])
+        return (v[len(v) // 2], v[0], v[-1]) if v else (None, None, None)
+
+    c50, c_lo, c_hi = stats(mhz)
+    w50, w_lo, w_hi = stats(watts)
+    limit = num(first_pwr.get("power_limit"))
+    return {"gfx_mhz_median": c50, "gfx_mhz_min": c_lo, "gfx_mhz_max": c_hi,
+            "socket_power_w_median": w50, "socket_power_w_min": w_lo, "socket_power_w_max": w_hi,
+            "power_limit_w": limit / 1e6 if limit and limit > 1e5 else limit,
+            "samples": len(mhz), "driver_max_mhz": first_clk.get("max_clk"),
+            "locked": first_clk.get("clk_locked"), "pinned": False,
+            "note": "sampled while the headline forward runs back to back; peaks are quoted at "
+                    "2400 MHz; clocks cannot be pinned without root"}
 
 
 def _cpu_model():
