@@ -394,7 +394,7 @@ def main():
         "ms": round(avg, 4), "value": round(flops / (avg * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
         "frac_fp32_peak": round(flops / (avg * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
         "flop_per_call": flops,
-        "note": "one 128-row query tile per 4-wave workgroup, 4 workgroups: latency-bound"}
+        "note": "16 workgroups of 32 query rows, 8 waves each over an eighth of the keys, merged in LDS: latency-bound"}
     # Clocks cannot be pinned without administrator rights; the GFX clock is
     # sampled while the headline forward runs back to back instead.
     result["clock"] = _gfx_clock_during(

@@ -90,8 +90,12 @@ eta::FwdPlan plan_fwd(int B, int H, int Nq, int d, bool bf16) {
   } else {
     p.waves = 4;
     p.block_keys = 32;
+    // Fewer 128-row tiles than CUs: 32-row workgroups whose waves (8 at
+    // d = 64, 4 at d = 128) split the keys (each wave's chain of fp32 MFMAs
+    // is the latency there).
+    if ((long long)B * H * ((Nq + 127) / 128) < kNumCU) p.key_parts = d == 64 ? 8 : 4;
   }
-  p.block_rows = p.rows_per_wave * p.waves;
+  p.block_rows = p.key_parts > 1 ? p.rows_per_wave : p.rows_per_wave * p.waves;
   p.workgroups = (long long)B * H * ((Nq + p.block_rows - 1) / p.block_rows);
   return p;
 }
@@ -660,13 +664,21 @@ int attn_plan_describe(int phase, int B, int H, int Hkv, int Nq, int Nk, int d, 
     if (check_fwd_shape(B, H, Hkv, Nq, Nk, d, 1.f, dtype) != ATTN_OK) return -1;
     const bool bf16 = dtype == ATTN_DTYPE_BF16;
     eta::FwdPlan p = plan_fwd(B, H, Nq, d, bf16);
-    n = snprintf(tmp, sizeof(tmp),
-                 "phase=fwd kernel=%s d=%d causal=%d Br=%d (%d waves x %d rows) Bc=%d "
-                 "grid=%lld workgroups (B*H*ceil(Nq/Br)) order=heavy-query-tiles-first "
-                 "head-interleaved",
-                 bf16 ? "fwd_bf16_mfma32x32x16" : "fwd_f32_mfma32x32x2",
-                 d, causal ? 1 : 0, p.block_rows, p.waves, p.rows_per_wave, p.block_keys,
-                 p.workgroups);
+    if (p.key_parts > 1)
+      n = snprintf(tmp, sizeof(tmp),
+                   "phase=fwd kernel=fwd_f32_keysplit_mfma32x32x2 d=%d causal=%d Br=%d "
+                   "(%d waves split the keys of %d rows, merged in LDS) Bc=%d grid=%lld "
+                   "workgroups (B*H*ceil(Nq/Br)) order=heavy-query-tiles-first",
+                   d, causal ? 1 : 0, p.block_rows, p.key_parts, p.rows_per_wave, p.block_keys,
+                   p.workgroups);
+    else
+      n = snprintf(tmp, sizeof(tmp),
+                   "phase=fwd kernel=%s d=%d causal=%d Br=%d (%d waves x %d rows) Bc=%d "
+                   "grid=%lld workgroups (B*H*ceil(Nq/Br)) order=heavy-query-tiles-first "
+                   "head-interleaved",
+                   bf16 ? "fwd_bf16_mfma32x32x16" : "fwd_f32_mfma32x32x2",
+                   d, causal ? 1 : 0, p.block_rows, p.waves, p.rows_per_wave, p.block_keys,
+                   p.workgroups);
   } else if (phase == ATTN_PHASE_DECODE) {
     if (check_decode_shape(B, H, Hkv, d, 16, 1, (Nk + 15) / 16 > 0 ? (Nk + 15) / 16 : 1, Nk, 0) !=
         ATTN_OK)

@@ -805,6 +805,204 @@ __global__ __launch_bounds__(NW * 64) void fwd_f32_kernel(
   }
 }
 
+// fp32 path for small grids: one workgroup per 32 query rows, its NW
+// waves splitting the key range (wave w takes key tiles w, w + NW, ...), each
+// with its own running (m, l, o) for the same rows, merged through LDS at the
+// end with the split-context algebra of "Attention kernels", FlashDecoding
+// paragraph: M = max_w m_w, l = sum_w 2^(m_w - M) l_w, O = sum_w 2^(m_w - M)
+// o_w / l.  With few query rows the per-tile chain of fp32 MFMAs is the
+// latency; splitting the keys NW ways shortens it.  Each wave stages
+// its own K tile, then its V tile, in a private slice of LDS.  Operand
+// layouts as in fwd_f32_kernel.
+template <int D, bool CAUSAL, int NW, bool PREFETCH>
+__global__ __launch_bounds__(NW * 64) void fwd_f32_ksplit_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int B, int H, int Hkv, int Nq, int Nk,
+    float scale_log2, int n_rtiles) {
+  constexpr int BC = 32;
+  constexpr int CH = D / 4;   // 16-byte chunks per fp32 row
+  constexpr int LOADS = BC * CH / 64;
+  constexpr int KK = D / 8;
+  constexpr int NB = D / 32;
+
+  __shared__ __attribute__((aligned(16))) float slice[NW][BC * D];  // K, then V, then o
+  __shared__ float part_m[NW][32];
+  __shared__ float part_l[NW][32];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 31;
+  const int hh = lane >> 5;
+
+  const int BH = B * H;
+  const int rt = n_rtiles - 1 - (int)blockIdx.x / BH;  // heavy (late) row tiles first
+  const int bh = (int)blockIdx.x % BH;
+  const int b = bh / H;
+  const int h = bh % H;
+  const int g = h / (H / Hkv);
+  const int q0 = rt * 32;
+  const int off = Nk - Nq;
+  const int qrow = q0 + li;
+
+  const float* Qp = Q + ((size_t)b * H + h) * (size_t)Nq * D;
+  const float* Kp = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+  const float* Vp = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+  float* tile = slice[wave];
+
+  int n_tiles;
+  if (CAUSAL) {
+    const int last = min(Nk - 1, q0 + 31 + off);
+    n_tiles = last < 0 ? 0 : last / BC + 1;
+  } else {
+    n_tiles = (Nk + BC - 1) / BC;
+  }
+
+  f32x4 qf[KK];
+  {
+    const bool ok = qrow < Nq;
+    const float* src = Qp + (size_t)(ok ? qrow : 0) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = ok ? *(const f32x4*)(src + 8 * kk + 4 * hh) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  f32x16 o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // K and V rows of key tile t into registers (rows past Nk as zeros).
+  f32x4 kv[LOADS], vv[LOADS];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int cid = lane + it * 64;
+      const int key = t * BC + cid / CH;
+      const int c = cid % CH;
+      kv[it] = vv[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t < n_tiles && key < Nk) {
+        kv[it] = *(const f32x4*)(Kp + (size_t)key * D + c * 4);
+        vv[it] = *(const f32x4*)(Vp + (size_t)key * D + c * 4);
+      }
+    }
+  };
+  if (PREFETCH) fetch(wave);
+  for (int t = wave; t < n_tiles; t += NW) {
+    const int k0 = t * BC;
+    // This tile's K goes to the slice now, its V after the scores (the
+    // wave's LDS accesses run in program order); with PREFETCH the next
+    // tile's rows are fetched meanwhile.
+    if (!PREFETCH) fetch(t);
+    f32x4 vcur[LOADS];
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) vcur[it] = vv[it];
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int cid = lane + it * 64;
+      const int row = cid / CH;
+      const int c = cid % CH;
+      *(f32x4*)(&tile[row * D + ((c ^ (row & (CH - 1))) * 4)]) = kv[it];
+    }
+    if (PREFETCH) fetch(t + NW);
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int c = 2 * kk + hh;
+      const f32x4 a = *(const f32x4*)(&tile[li * D + ((c ^ (li & (CH - 1))) * 4)]);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) s = mfma32_f32(a[tt], qf[kk][tt], s);
+    }
+    const bool need_mask = (k0 + BC > Nk) || (CAUSAL && (k0 + BC - 1 > q0 + off));
+    if (need_mask) {
+      const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key > lim) s[r] = -INFINITY;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -m_use));
+      s[r] = p;
+      rs += p;
+    }
+    l_run = alpha * l_run + rs;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+      const int cid = lane + it * 64;
+      *(f32x4*)(&tile[(cid / CH) * D + (cid % CH) * 4]) = vcur[it];
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+        o[nb] = mfma32_f32(tile[key * D + 32 * nb + li], s[r], o[nb]);
+      }
+  }
+
+  // Publish this wave's partial: o as rows of its slice, m and l per row.
+  const float l_tot = l_run + swap_halves(l_run);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = o[nb][4 * r4 + e];
+      *(f32x4*)(&tile[li * D + 32 * nb + 8 * r4 + 4 * hh]) = w;
+    }
+  if (hh == 0) {
+    part_m[wave][li] = m_run;
+    part_l[wave][li] = l_tot;
+  }
+  __syncthreads();
+
+  // Merge: the workgroup's threads take the 32 rows' 16-byte chunks in turn.
+  constexpr int ITEMS = 32 * CH;
+#pragma unroll
+  for (int i0 = 0; i0 < ITEMS; i0 += NW * 64) {
+    const int i = i0 + (int)threadIdx.x;
+    if (ITEMS % (NW * 64) != 0 && i >= ITEMS) break;
+    const int r = i / CH;
+    const int c = i % CH;
+    const int row = q0 + r;
+    float big_m = part_m[0][r];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) big_m = fmaxf(big_m, part_m[w][r]);
+    const float m_ref = big_m == -INFINITY ? 0.f : big_m;
+    float ell = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = fast_exp2(part_m[w][r] - m_ref);
+      ell += wt * part_l[w][r];
+      acc += wt * *(const f32x4*)(&slice[w][r * D + c * 4]);
+    }
+    if (row < Nq) {
+      const float inv = ell > 0.f ? 1.f / ell : 0.f;
+      *(f32x4*)(O + (((size_t)b * H + h) * (size_t)Nq + row) * D + c * 4) = acc * inv;
+      if (c == 0)
+        LSE[((size_t)b * H + h) * (size_t)Nq + row] =
+            ell > 0.f ? (big_m + fast_log2(ell)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
 template <int D, bool BAND>
 hipError_t launch_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
   constexpr int BC = fwd_bc<D>();
@@ -864,7 +1062,22 @@ hipError_t launch_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_f32(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_f32(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
+  if (p.key_parts > 1) {
+    // d = 64: eight waves (two per SIMD, each covering the other's
+    // latencies); d = 128: four waves, each fetching its next tile's rows
+    // ahead (two waves would not fit the registers).  Single head, 512 keys:
+    // d = 64 with four waves and prefetch 17.0 us, eight without 15.3 us,
+    // eight with 16.0 us, sixteen 28.8 us.
+    constexpr int NWK = D == 64 ? 8 : 4;
+    constexpr bool PF = D != 64;
+    const int n_rtiles = (a.Nq + 31) / 32;
+    hipLaunchKernelGGL((fwd_f32_ksplit_kernel<D, CAUSAL, NWK, PF>),
+                       dim3((unsigned)(n_rtiles * a.B * a.H)), dim3(NWK * 64), 0, stream,
+                       (const float*)a.Q, (const float*)a.K, (const float*)a.V, (float*)a.O,
+                       a.LSE, a.B, a.H, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_rtiles);
+    return hipGetLastError();
+  }
   constexpr int NW = 4;
   const int n_qtiles = (a.Nq + NW * 32 - 1) / (NW * 32);
   dim3 grid((unsigned)(n_qtiles * a.B * a.H));
@@ -883,8 +1096,8 @@ hipError_t launch_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
     return a.band ? launch_bf16<64, true>(a, p, stream) : launch_bf16<64, false>(a, p, stream);
   }
   if (a.d == 128)
-    return a.causal ? launch_f32<128, true>(a, stream) : launch_f32<128, false>(a, stream);
-  return a.causal ? launch_f32<64, true>(a, stream) : launch_f32<64, false>(a, stream);
+    return a.causal ? launch_f32<128, true>(a, p, stream) : launch_f32<128, false>(a, p, stream);
+  return a.causal ? launch_f32<64, true>(a, p, stream) : launch_f32<64, false>(a, p, stream);
 }
 
 }  // namespace eta

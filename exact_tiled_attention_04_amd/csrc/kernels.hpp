@@ -99,6 +99,7 @@ struct FwdPlan {
   int block_rows;   // query rows per workgroup
   int block_keys;   // keys per K/V tile
   long long workgroups;
+  int key_parts = 1;  // > 1: the waves of a workgroup split the keys of the same rows (fp32)
 };
 
 struct DecodeArgs {

@@ -189,6 +189,11 @@ def test_plan_describe_per_phase(lib):
     assert "phase=fwd" in fwd and "Br=128" in fwd and "grid=2048" in fwd
     small = attn.attn_plan_describe(attn.ATTN_PHASE_FWD, 1, 4, 4, 8192, 8192, 128, True)
     assert "Br=64" in small  # too few workgroups at Br=128: split the sequence finer
+    f32 = attn.ATTN_DTYPE_F32
+    one = attn.attn_plan_describe(attn.ATTN_PHASE_FWD, 1, 1, 1, 512, 512, 64, False, f32)
+    assert "fwd_f32_keysplit" in one and "Br=32" in one and "grid=16" in one
+    wide = attn.attn_plan_describe(attn.ATTN_PHASE_FWD, 2, 16, 16, 1030, 1030, 128, True, f32)
+    assert "fwd_f32_mfma32x32x2" in wide and "Br=128" in wide and "grid=288" in wide
     dec = attn.attn_plan_describe(attn.ATTN_PHASE_DECODE, 64, 32, 8, 1, 32768, 128, False)
     assert "phase=decode" in dec and "G=4" in dec
     bwd = attn.attn_plan_describe(attn.ATTN_PHASE_BWD, 2, 16, 16, 4096, 4096, 128, True)

@@ -34,6 +34,29 @@ def test_single_head_f32_n512_d64(gpu):
     _run(gpu, 1, 1, 1, 512, 512, 64, "f32", False, seed=0, scale=1.0 / 8.0)
 
 
+F32_PATHS = [
+    # (B, H, Nq, Nk): fewer 128-row tiles than CUs -> key-split kernel
+    # (32-row workgroups, four waves over the keys, merged in LDS) ...
+    (1, 1, 512, 512), (1, 3, 33, 33), (2, 2, 17, 200), (1, 2, 200, 17), (1, 1, 1, 1),
+    (1, 1, 31, 1000),
+    # ... otherwise the 128-row kernel.
+    (2, 16, 1030, 1030),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk", F32_PATHS)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_both_kernels(gpu, B, H, Nq, Nk, d, causal):
+    """fp32 on both of its kernels (the plan names which one runs), every
+    row against the oracle: ragged tiles, fewer key tiles than waves, Nq > Nk
+    (rows with no visible key when causal)."""
+    plan = attn.attn_plan_describe(attn.ATTN_PHASE_FWD, B, H, H, Nq, Nk, d, causal,
+                                   attn.ATTN_DTYPE_F32)
+    assert ("keysplit" in plan) == (B * H * -(-Nq // 128) < 256)
+    _run(gpu, B, H, H, Nq, Nk, d, "f32", causal, seed=Nq + Nk + d)
+
+
 def test_causal_bf16_b4_h16_n2048_d64(gpu):
     """bf16 causal prefill, B=4, H=16, N=2048, d=64, scale 1/8 (full oracle)."""
     _run(gpu, 4, 16, 16, 2048, 2048, 64, "bf16", True, seed=0, scale=1.0 / 8.0)
