@@ -266,6 +266,10 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # amdsmi's readings lag by hundreds of milliseconds, longer than the
+    # timed steps: the clock and power are sampled over two further seconds
+    # of the same steps, run back to back right after them.
+    clock = _clock_during(step, stream)
 
     def med(vals):
         s = sorted(vals)
@@ -395,10 +399,9 @@ def main():
         "frac_fp32_peak": round(flops / (avg * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
         "flop_per_call": flops,
         "note": "16 workgroups of 32 query rows, 8 waves each over an eighth of the keys, merged in LDS: latency-bound"}
-    # Clocks cannot be pinned without administrator rights; the GFX clock is
-    # sampled while the headline forward runs back to back instead.
-    result["clock"] = _gfx_clock_during(
-        lambda: attn.attn_fwd(q, k, v, fw["scale"], True, out=o, lse=lse, stream=stream))
+    # Clocks cannot be pinned without administrator rights; the GFX clock and
+    # socket power are sampled while the timed steps run.
+    result["clock"] = clock
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, fw, args.cpu_heads)
     print(json.dumps(result))
@@ -537,13 +540,14 @@ def _sparse_pairs(row_ptr, col_idx, block=128):
     return pairs
 
 
-def _gfx_clock_during(call, seconds=1.0):
+def _clock_during(call, stream, seconds=2.0):
     """GFX clock and socket power (amdsmi clock and power queries) sampled
-    while `call` runs back to back: batches of calls are queued and both are
-    read while they run.  Returns the median and range over the samples
-    after the first quarter (settling), the board's power limit, or the
-    error.  (amdsmi's GPU-metrics table is not used: it held the same stale
-    idle values for the whole run.)"""
+    while `call` runs back to back on `stream`: batches of calls are queued,
+    two batches stay in flight (so the GPU never waits for the host), and
+    both values are read while they run.  Returns the median and range over
+    the second half of the samples (amdsmi's readings lag by hundreds of
+    milliseconds), the board's power limit, or the error.  (amdsmi's GPU-metrics table is not used: it held the same
+    stale idle values for the whole run.)"""
     import torch
     try:
         import amdsmi
@@ -562,10 +566,16 @@ def _gfx_clock_during(call, seconds=1.0):
             return None
 
     mhz, watts = [], []
+    in_flight = []
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
-        for _ in range(8):
+        for _ in range(4):
             call()
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        in_flight.append(ev)
+        if len(in_flight) > 2:
+            in_flight.pop(0).synchronize()
         try:
             c = num(clk().get("clk"))
             w = num(pwr().get("current_socket_power"))
@@ -575,14 +585,14 @@ def _gfx_clock_during(call, seconds=1.0):
                 watts.append(w)
         except Exception:
             pass
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
     try:
         amdsmi.amdsmi_shut_down()
     except Exception:
         pass
 
     def stats(v):
-        v = sorted(v[len(v) // 4:])
+        v = sorted(v[len(v) // 2:])
         return (v[len(v) // 2], v[0], v[-1]) if v else (None, None, None)
 
     c50, c_lo, c_hi = stats(mhz)
@@ -593,8 +603,8 @@ def _gfx_clock_during(call, seconds=1.0):
             "power_limit_w": limit / 1e6 if limit and limit > 1e5 else limit,
             "samples": len(mhz), "driver_max_mhz": first_clk.get("max_clk"),
             "locked": first_clk.get("clk_locked"), "pinned": False,
-            "note": "sampled while the headline forward runs back to back; peaks are quoted at "
-                    "2400 MHz; clocks cannot be pinned without root"}
+            "note": "sampled over the second of two seconds of the same steps run back to back "
+                    "after the timed ones; peaks are quoted at 2400 MHz; clocks cannot be pinned without root"}
 
 
 def _cpu_model():
