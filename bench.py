@@ -17,8 +17,8 @@ device synchronisation on both sides.  Rank 0 prints one JSON line.
 After the timed steps, the other forward configurations (d = 64: B=4, H=16,
 N=2048 causal; the headline shape non-causal) and the entry points beyond the
 hot path are timed the same way in a loop of their own (K calls each, after W
-warm-up calls), so they do not change the conditions the step is measured
-under:
+warm-up calls and 0.3 s of further calls), so they do not change the
+conditions the step is measured under:
   * the 4-head variant of (1) through the key split;
   * a packed ragged causal prefill (16 sequences of 512..8192 tokens, GQA
     32/8, d=128);
@@ -55,7 +55,10 @@ def _parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # A GPU coming out of idle runs these kernels ~5% slower for its first
+    # tens to hundreds of milliseconds while its clocks and power settle;
+    # 400 warm-up steps (~0.7 s) put the timed steps in the steady state.
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the fp64 oracle on the host (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -275,11 +278,11 @@ def main():
         s = sorted(vals)
         return s[len(s) // 2]
 
-    # Each one after W warm-up calls and 30 ms of further calls, so it runs
-    # at the clock its own load settles at rather than its predecessor's.
+    # Each one after a few warm-up calls and 0.3 s of further calls, so it
+    # runs at the clock its own load settles at rather than its predecessor's.
     extra = {}
     for name, flops, call in extras:
-        ms = _time_calls(call, stream, args.steps, args.warmup)
+        ms = _time_calls(call, stream, args.steps, min(args.warmup, 3), settle_s=0.3)
         extra[name] = (sum(ms) / len(ms), med(ms), flops, ms)
 
     fwd_ms = [ev[0].elapsed_time(ev[1]) for ev in events]
