@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "../../include/attn.h"
 #include "kernels.hpp"
@@ -182,9 +183,10 @@ attn_status_t check_bwd_shape(int B, int H, int Hkv, int Nq, int Nk, int d, floa
 // too few independent workgroups leave CUs idle; "Attention kernels",
 // FlashDecoding paragraph: split the key range and merge the partials).
 // When B*H*ceil(Nq/128) query tiles give fewer than two workgroups per CU,
-// each tile's key range is cut into equal parts sized for about four units
-// per CU in total (at least 640 keys each).  chunk_keys > 0 forces the part
-// size.
+// each tile's key range is cut into equal parts: the shortest parts (of at
+// least 640 keys) whose units all fit the split kernel's resident
+// workgroups at once (three per CU at d = 128, four at d = 64).  chunk_keys
+// > 0 forces the part size.
 struct SplitPlan {
   int chunk_tiles = 0;
   int n_chunks = 0;      // most parts of any query tile; 0: no split
@@ -203,25 +205,40 @@ SplitPlan plan_fwd_split(int B, int H, int Nq, int Nk, int d, int left, int righ
     ct = (chunk_keys + bc - 1) / bc;
   } else {
     if ((long long)B * H * n_qt >= 2LL * kNumCU) return sp;
-    long long work = 0;
+    // One round of units: measured at 4 heads x 8k causal (d = 128), parts
+    // of 1664 keys (760 units for 768 resident workgroups) run 85 us, while
+    // 1536 keys (816 units: 48 wait for a second round) run 101 us and 1056
+    // keys (1136 units) 91 us; fewer units than slots leave CUs idle
+    // (2048 keys, 640 units: 93 us).  Parts shorter than 640 keys pay more
+    // partial traffic and merge work than they gain in balance.
+    std::vector<int> len;
+    len.reserve(n_qt);
+    int longest = 0;
     for (int qt = 0; qt < n_qt; ++qt) {
       int lo, hi;
       eta::band_tiles(band, qt * 128, 128, Nq, Nk, bc, left, right, lo, hi);
-      if (hi >= lo) work += hi - lo + 1;
+      len.push_back(hi >= lo ? hi - lo + 1 : 0);
+      longest = len.back() > longest ? len.back() : longest;
     }
-    work *= (long long)B * H;
-    // About four units per CU, parts of at least 640 keys: shorter parts pay
-    // more partial traffic and merge work than they gain in balance (4 heads
-    // x 4k causal: 288-key parts 352-365 TFLOP/s, 640-key parts 433-446; the
-    // larger grids swept, 1-4 heads of 8k-32k, sit within 2% of their best
-    // part size).
-    const long long target = 4LL * kNumCU;
-    ct = (int)((work + target - 1) / target);
-    if (ct < 640 / bc) ct = 640 / bc;
+    const long long slots = (long long)kNumCU * (d == 128 ? 3 : 4);
+    auto units_for = [&](int c) {
+      long long u = 0;
+      for (int t : len) u += (t + c - 1) / c;
+      return u * B * H;
+    };
+    // units_for falls as the part size grows; at the longest range every
+    // tile is one unit, and B*H*n_qt < 2 * kNumCU <= slots.
+    int lo = 640 / bc, hi = longest > lo ? longest : lo;
+    if (units_for(lo) <= slots) {
+      ct = lo;
+    } else {
+      while (hi - lo > 1) {
+        const int mid = lo + (hi - lo) / 2;
+        if (units_for(mid) <= slots) hi = mid; else lo = mid;
+      }
+      ct = hi;
+    }
   }
-  const int n_tiles = (Nk + bc - 1) / bc;
-  int n_chunks = (n_tiles + ct - 1) / ct;
-  if (n_chunks <= 1 && chunk_keys == 0) return sp;
   // Exact number of (query tile, part) units: the grid holds one workgroup
   // per unit and head, with no idle slots (workgroups reach the XCDs round
   // robin, so idle slots in a fixed pattern would unbalance them).
@@ -234,7 +251,8 @@ SplitPlan plan_fwd_split(int B, int H, int Nq, int Nk, int d, int left, int righ
     units += parts;
     if (parts > max_parts) max_parts = parts;
   }
-  n_chunks = max_parts > 0 ? max_parts : 1;
+  if (max_parts <= 1 && chunk_keys == 0) return sp;  // every tile in one part
+  const int n_chunks = max_parts > 0 ? max_parts : 1;
   sp.units = units;
   sp.chunk_tiles = ct;
   sp.n_chunks = n_chunks;

@@ -273,12 +273,14 @@ void fwd_bf16_kernel(
   // causal and local masks change the visited tile range).
   int t_lo, t_hi;
   band_tiles(BAND, q0, BR, Nq, Nk, BC, win_left, win_right, t_lo, t_hi);
+  int parts = 1;
   if (SPLIT) {
     // This workgroup's share of the key range ("Attention kernels",
     // FlashDecoding paragraph, applied to a prefill query tile): the tile's
     // key tiles cut into equal parts of at most chunk_tiles tiles.  An empty
     // share exits before any barrier (the condition is uniform over the
-    // workgroup).
+    // workgroup).  A tile of one part is written like an unsplit one.
+    parts = (t_hi - t_lo + chunk_tiles) / chunk_tiles;
     if (!split_part(t_lo, t_hi, chunk_tiles, chunk)) return;
   }
 
@@ -562,7 +564,7 @@ void fwd_bf16_kernel(
   }
 
   const float l_tot = halves_sum(l_run);
-  if (SPLIT) {
+  if (SPLIT && parts > 1) {
     // Unnormalised partial: o (as whole rows through the wave's slice of the
     // idle K/V buffers), the base-2 reference max and the sum, merged by
     // fwd_merge_kernel.
@@ -595,9 +597,10 @@ void fwd_bf16_kernel(
 // Merge of the key-split partials of each query row (the split-context
 // algebra of "Attention kernels", FlashDecoding paragraph): M = max_c m_c,
 // w_c = 2^(m_c - M), l = sum_c w_c l_c, O = sum_c w_c o_c / l,
-// LSE = (M + log2 l) ln 2.  D/4 threads per row, four columns each (16-byte
-// loads), 256 / (D/4) rows per workgroup; the partial loads are issued eight
-// chunks at a time.
+// LSE = (M + log2 l) ln 2.  A tile of one part was written by its unit and
+// is skipped.  D/4 threads per row, four columns each (16-byte loads),
+// 256 / (D/4) rows per workgroup; the partial loads are issued eight chunks
+// at a time.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(
     const float* __restrict__ part, __bf16* __restrict__ O, float* __restrict__ LSE, int BH,
@@ -616,6 +619,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
   int t_lo, t_hi;
   band_tiles(band != 0, qt * BR, BR, Nq, Nk, BC, win_left, win_right, t_lo, t_hi);
   const int parts = t_lo <= t_hi ? (t_hi - t_lo + chunk_tiles) / chunk_tiles : 0;
+  if (parts == 1) return;
   const size_t row0 = ((size_t)bh * n_qtiles + qt) * n_chunks * BR + row % BR;
   const float* ml = part + (size_t)BH * n_qtiles * n_chunks * BR * D;
   float big_m = -INFINITY, ell = 0.f;

@@ -234,6 +234,15 @@ def test_bwd_local_validation(lib, cpu_only):
     assert st == attn.ATTN_ERR_WORKSPACE
 
 
+def _one_round_part(tiles, heads, slots, least):
+    """Smallest part size in key tiles (at least `least`) whose parts of
+    every query tile of every head number at most `slots`, by enumeration."""
+    c = least
+    while heads * sum(-(-t // c) for t in tiles) > slots:
+        c += 1
+    return c
+
+
 def test_fwd_splitkv_workspace_queries(lib):
     # Forced 256-key parts over 1000 causal keys of d = 128 (32-key tiles): the
     # last query tile sees 1000 keys = 32 tiles = 4 parts of 8 tiles.
@@ -241,7 +250,22 @@ def test_fwd_splitkv_workspace_queries(lib):
         2 * 8 * 4 * 128 * 130 * 4
     assert attn.attn_fwd_splitkv_workspace_size(1, 2, 1000, 1000, 128, -1, 0, 100) == 0
     assert attn.attn_fwd_splitkv_workspace_size(1, 32, 8192, 8192, 128, -1, 0, 0) == 0
-    assert attn.attn_fwd_splitkv_workspace_size(1, 4, 8192, 8192, 128, -1, 0, 0) > 0
+    # Planner, 4 heads x 8192 causal at d = 128: query tile i sees 4 (i + 1)
+    # key tiles; parts of 52 tiles (1664 keys) are the shortest whose 760
+    # units fit the 768 resident workgroups (3 per CU); the last tile has 5.
+    tiles = [4 * (i + 1) for i in range(64)]
+    ct = _one_round_part(tiles, 4, 3 * 256, 20)
+    assert ct == 52
+    assert attn.attn_fwd_splitkv_workspace_size(1, 4, 8192, 8192, 128, -1, 0, 0) == \
+        4 * 64 * -(-256 // ct) * 128 * 130 * 4
+    # d = 64 (64-key tiles, 4 resident workgroups per CU), 4 heads x 4096.
+    tiles = [2 * (i + 1) for i in range(32)]
+    ct = _one_round_part(tiles, 4, 4 * 256, 10)
+    assert attn.attn_fwd_splitkv_workspace_size(1, 4, 4096, 4096, 64, -1, 0, 0) == \
+        4 * 32 * -(-64 // ct) * 128 * 66 * 4
+    # One 128-row query tile against 512 keys: parts of at least 640 keys
+    # would not split it.
+    assert attn.attn_fwd_splitkv_workspace_size(1, 1, 128, 512, 128, -1, 0, 0) == 0
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -78,3 +78,39 @@ def test_causal_bf16_b1_h4_n8192_d128_split(gpu):
         o_ref, lse_ref = oracle.forward(to64(q[sl]), to64(k[sl]), to64(v[sl]), scale, True)
         check_out(to64(o[sl]), o_ref, "bf16", what=f"O head {h}")
         check_lse(to64(lse[sl]), lse_ref, "bf16", what=f"LSE head {h}")
+
+
+@pytest.mark.parametrize("fill", [0x00, 0xFF])
+def test_workspace_reuse_repeatable(gpu, fill):
+    """A workspace holding any bytes, reused by calls of other sizes and part
+    sizes, gives the oracle's result, and repeated calls are bit-identical
+    (each tile's partials merge in part order)."""
+    ws = torch.full((attn.attn_fwd_splitkv_workspace_size(1, 3, 1000, 1000, 128, -1, 0, 128),),
+                    fill, dtype=torch.uint8, device=gpu)
+    for N, chunk in ((1000, 1024), (777, 128), (1000, 128)):
+        assert ws.numel() >= attn.attn_fwd_splitkv_workspace_size(1, 3, N, N, 128, -1, 0, chunk)
+        q, k, v = workloads.prefill(1, 3, 1, N, N, 128, dtype="bf16", seed=N + chunk + fill)
+        qg, kg, vg = q.to(gpu), k.to(gpu), v.to(gpu)
+        o1, l1 = attn.attn_fwd_splitkv(qg, kg, vg, 0.09, -1, 0, chunk_keys=chunk, workspace=ws)
+        o2, l2 = attn.attn_fwd_splitkv(qg, kg, vg, 0.09, -1, 0, chunk_keys=chunk, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"N={N}: repeated calls differ"
+        o_ref, lse_ref = oracle.forward(to64(q), to64(k), to64(v), 0.09, True)
+        check_out(to64(o1), o_ref, "bf16", what=f"O N={N} chunk={chunk}")
+        check_lse(to64(l1), lse_ref, "bf16", what=f"LSE N={N} chunk={chunk}")
+
+
+def test_planner_split_d64(gpu):
+    """The planner's split at d = 64 (64-key tiles; 4 heads x 4096 causal:
+    parts of 640 keys, 476 units): every row against the oracle."""
+    B, H, N, d = 1, 4, 4096, 64
+    assert attn.attn_fwd_splitkv_workspace_size(B, H, N, N, d, -1, 0, 0) > 0
+    q, k, v = workloads.prefill(B, H, H, N, N, d, dtype="bf16", seed=5, device=str(gpu))
+    o, lse = attn.attn_fwd_splitkv(q, k, v, 0.125, -1, 0)
+    torch.cuda.synchronize()
+    q, k, v, o, lse = q.cpu(), k.cpu(), v.cpu(), o.cpu(), lse.cpu()
+    for h in range(H):
+        sl = (slice(0, 1), slice(h, h + 1))
+        o_ref, lse_ref = oracle.forward(to64(q[sl]), to64(k[sl]), to64(v[sl]), 0.125, True)
+        check_out(to64(o[sl]), o_ref, "bf16", what=f"O head {h}")
+        check_lse(to64(lse[sl]), lse_ref, "bf16", what=f"LSE head {h}")
