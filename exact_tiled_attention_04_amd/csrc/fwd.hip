@@ -598,9 +598,9 @@ void fwd_bf16_kernel(
 // algebra of "Attention kernels", FlashDecoding paragraph): M = max_c m_c,
 // w_c = 2^(m_c - M), l = sum_c w_c l_c, O = sum_c w_c o_c / l,
 // LSE = (M + log2 l) ln 2.  A tile of one part was written by its unit and
-// is skipped.  D/4 threads per row, four columns each (16-byte loads),
-// 256 / (D/4) rows per workgroup; the partial loads are issued eight chunks
-// at a time.
+// is skipped.  D/4 threads per row, four columns each (16-byte loads); each
+// thread takes two rows 256 / (D/4) apart, with up to eight parts' loads of
+// both in flight.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(
     const float* __restrict__ part, __bf16* __restrict__ O, float* __restrict__ LSE, int BH,
@@ -609,55 +609,76 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
   constexpr int BR = 128;
   constexpr int BC = fwd_bc<D>();
   constexpr int TPR = D / 4;
-  constexpr int RPB = 256 / TPR;
+  constexpr int RPP = 256 / TPR;  // rows per pass of the workgroup
+  constexpr int PR = 2;           // rows per thread, their loads in flight together
   constexpr int kBatch = 8;
+  static_assert(BR % (PR * RPP) == 0, "a workgroup's rows lie in one query tile");
   const int bh = blockIdx.y;
-  const int row = blockIdx.x * RPB + (int)threadIdx.x / TPR;
+  const int row_a = blockIdx.x * (PR * RPP) + (int)threadIdx.x / TPR;
   const int n4 = ((int)threadIdx.x % TPR) * 4;
-  if (row >= Nq) return;
-  const int qt = row / BR;
+  if (row_a >= Nq) return;
+  const int qt = row_a / BR;
   int t_lo, t_hi;
   band_tiles(band != 0, qt * BR, BR, Nq, Nk, BC, win_left, win_right, t_lo, t_hi);
-  const int parts = t_lo <= t_hi ? (t_hi - t_lo + chunk_tiles) / chunk_tiles : 0;
+  // Every part of a tile is non-empty: with p = ceil(n / chunk_tiles) parts
+  // of ceil(n / p) tiles, the last starts at (p - 1) ceil(n / p) < n.
+  int parts = t_lo <= t_hi ? (t_hi - t_lo + chunk_tiles) / chunk_tiles : 0;
   if (parts == 1) return;
-  const size_t row0 = ((size_t)bh * n_qtiles + qt) * n_chunks * BR + row % BR;
+  parts = min(parts, n_chunks);
   const float* ml = part + (size_t)BH * n_qtiles * n_chunks * BR * D;
-  float big_m = -INFINITY, ell = 0.f;
-  f32x4 acc = f32x4{};
-  for (int c0 = 0; c0 < parts; c0 += kBatch) {
-    float mv[kBatch], lv[kBatch];
-    f32x4 ov[kBatch];
+  const size_t tile0 = ((size_t)bh * n_qtiles + qt) * n_chunks * BR;
+  float big_m[PR], ell[PR];
+  f32x4 acc[PR];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      int lo = t_lo, hi = t_hi;
-      const bool ok = c0 + j < parts && split_part(lo, hi, chunk_tiles, c0 + j);
-      const size_t prow = row0 + (size_t)(ok ? c0 + j : 0) * BR;
-      mv[j] = ok ? ml[prow * 2] : -INFINITY;
-      lv[j] = ok ? ml[prow * 2 + 1] : 0.f;
-      ov[j] = ok ? *(const f32x4*)(part + prow * D + n4) : f32x4{};
-    }
-    float bm = big_m;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) bm = fmaxf(bm, mv[j]);
-    if (bm == -INFINITY) continue;
-    const float r = fast_exp2(big_m - bm);
-    acc *= r;
-    ell *= r;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const float w = fast_exp2(mv[j] - bm);
-      ell += w * lv[j];
-      acc += w * ov[j];
-    }
-    big_m = bm;
+  for (int i = 0; i < PR; ++i) {
+    big_m[i] = -INFINITY;
+    ell[i] = 0.f;
+    acc[i] = f32x4{};
   }
-  const float inv = ell > 0.f ? 1.f / ell : 0.f;
-  const size_t orow = (size_t)bh * Nq + row;
-  u32x2 w;
-  w[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  w[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  *(u32x2*)(O + orow * D + n4) = w;
-  if (n4 == 0) LSE[orow] = ell > 0.f ? (big_m + fast_log2(ell)) * kLn2 : -INFINITY;
+  for (int c0 = 0; c0 < parts; c0 += kBatch) {
+    float mv[PR][kBatch], lv[PR][kBatch];
+    f32x4 ov[PR][kBatch];
+#pragma unroll
+    for (int i = 0; i < PR; ++i)
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int row = row_a + i * RPP;
+        const bool ok = c0 + j < parts && row < Nq;
+        const size_t prow = tile0 + (size_t)(ok ? c0 + j : 0) * BR + (ok ? row % BR : 0);
+        mv[i][j] = ok ? ml[prow * 2] : -INFINITY;
+        lv[i][j] = ok ? ml[prow * 2 + 1] : 0.f;
+        ov[i][j] = ok ? *(const f32x4*)(part + prow * D + n4) : f32x4{};
+      }
+#pragma unroll
+    for (int i = 0; i < PR; ++i) {
+      float bm = big_m[i];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) bm = fmaxf(bm, mv[i][j]);
+      if (bm == -INFINITY) continue;
+      const float r = fast_exp2(big_m[i] - bm);
+      acc[i] *= r;
+      ell[i] *= r;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const float w = fast_exp2(mv[i][j] - bm);
+        ell[i] += w * lv[i][j];
+        acc[i] += w * ov[i][j];
+      }
+      big_m[i] = bm;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PR; ++i) {
+    const int row = row_a + i * RPP;
+    if (row >= Nq) continue;
+    const float inv = ell[i] > 0.f ? 1.f / ell[i] : 0.f;
+    const size_t orow = (size_t)bh * Nq + row;
+    u32x2 w;
+    w[0] = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
+    w[1] = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
+    *(u32x2*)(O + orow * D + n4) = w;
+    if (n4 == 0) LSE[orow] = ell[i] > 0.f ? (big_m[i] + fast_log2(ell[i])) * kLn2 : -INFINITY;
+  }
 }
 
 // fp32 path: the same tiling on v_mfma_f32_32x32x2f32 (P stays fp32).
@@ -1042,7 +1063,7 @@ hipError_t launch_bf16(const FwdArgs& a, const FwdPlan& p, hipStream_t stream) {
                        a.win_right, a.chunk_tiles, a.n_chunks, part, FwdSeqArgs{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    constexpr int rpb = 256 / (D / 4);
+    constexpr int rpb = 2 * (256 / (D / 4));
     hipLaunchKernelGGL((fwd_merge_kernel<D>),
                        dim3((unsigned)((a.Nq + rpb - 1) / rpb), (unsigned)(a.B * a.H)), dim3(256), 0,
                        stream, (const float*)part, o, a.LSE, a.B * a.H, a.Nq, a.Nk,
