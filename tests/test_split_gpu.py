@@ -114,3 +114,22 @@ def test_planner_split_d64(gpu):
         o_ref, lse_ref = oracle.forward(to64(q[sl]), to64(k[sl]), to64(v[sl]), 0.125, True)
         check_out(to64(o[sl]), o_ref, "bf16", what=f"O head {h}")
         check_lse(to64(lse[sl]), lse_ref, "bf16", what=f"LSE head {h}")
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d,left,right", [
+    (1, 2, 1, 3000, 3000, 128, -1, 0),      # ragged causal, planner parts
+    (2, 3, 3, 1500, 1500, 64, -1, -1),      # no mask, d = 64
+    (1, 8, 2, 512, 6000, 128, -1, 0),       # a query chunk against a longer context, GQA
+    (1, 4, 4, 2500, 2500, 128, 700, 0),     # local window
+])
+def test_planner_split_shapes(gpu, B, H, Hkv, Nq, Nk, d, left, right):
+    """Shapes whose query tiles leave CUs idle, through the planner's part
+    size (chunk_keys = 0): every row against the oracle."""
+    assert attn.attn_fwd_splitkv_workspace_size(B, H, Nq, Nk, d, left, right, 0) > 0
+    q, k, v = workloads.prefill(B, H, Hkv, Nq, Nk, d, dtype="bf16", seed=Nq + Nk + d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = attn.attn_fwd_splitkv(q.to(gpu), k.to(gpu), v.to(gpu), scale, left, right)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.forward(to64(q), to64(k), to64(v), scale, False, _band(left, right))
+    check_out(to64(o), o_ref, "bf16")
+    check_lse(to64(lse), lse_ref, "bf16")
