@@ -697,6 +697,16 @@ int attn_plan_describe(int phase, int B, int H, int Hkv, int Nq, int Nk, int d, 
                    bf16 ? "fwd_bf16_mfma32x32x16" : "fwd_f32_mfma32x32x2",
                    d, causal ? 1 : 0, p.block_rows, p.waves, p.rows_per_wave, p.block_keys,
                    p.workgroups);
+    // The key split attn_fwd_splitkv would take for the same shape.
+    const SplitPlan sp =
+        bf16 ? plan_fwd_split(B, H, Nq, Nk, d, eta::kUnbounded, causal ? 0 : eta::kUnbounded, 0)
+             : SplitPlan();
+    if (sp.n_chunks > 0 && n > 0 && n < (int)sizeof(tmp))
+      n += snprintf(tmp + n, sizeof(tmp) - n,
+                    "; splitkv: Br=128 parts of <= %d keys, %lld units per head in one round "
+                    "(grid=%lld), <= %d parts per query tile, then fwd_merge",
+                    sp.chunk_tiles * eta::fwd_tile_keys(d), sp.units, sp.units * B * H,
+                    sp.n_chunks);
   } else if (phase == ATTN_PHASE_DECODE) {
     if (check_decode_shape(B, H, Hkv, d, 16, 1, (Nk + 15) / 16 > 0 ? (Nk + 15) / 16 : 1, Nk, 0) !=
         ATTN_OK)

@@ -187,8 +187,13 @@ def test_workspace_queries(lib):
 def test_plan_describe_per_phase(lib):
     fwd = attn.attn_plan_describe(attn.ATTN_PHASE_FWD, 1, 32, 32, 8192, 8192, 128, True)
     assert "phase=fwd" in fwd and "Br=128" in fwd and "grid=2048" in fwd
+    assert "splitkv" not in fwd  # the grid fills the GPU: no key split
     small = attn.attn_plan_describe(attn.ATTN_PHASE_FWD, 1, 4, 4, 8192, 8192, 128, True)
     assert "Br=64" in small  # too few workgroups at Br=128: split the sequence finer
+    # ... and the key split attn_fwd_splitkv takes: 1664-key parts, 190 units
+    # per head (760 workgroups for 768 resident), at most 5 parts per tile.
+    assert "splitkv: Br=128 parts of <= 1664 keys, 190 units per head" in small
+    assert "grid=760" in small and "<= 5 parts" in small
     f32 = attn.ATTN_DTYPE_F32
     one = attn.attn_plan_describe(attn.ATTN_PHASE_FWD, 1, 1, 1, 512, 512, 64, False, f32)
     assert "fwd_f32_keysplit" in one and "Br=32" in one and "grid=16" in one
