@@ -470,15 +470,20 @@ void fwd_bf16_kernel(
           (BAND && (k0 + BC - 1 > wave_row_lo + off + win_right ||
                     k0 < wave_row_lo + 31 + off - win_left));
       if (need_mask) {
-        const int lim = BAND ? min(Nk - 1, qrow + off + win_right) : Nk - 1;
-        const int lim_lo = BAND ? qrow + off - win_left : 0;
+        // Score r of block kb is key k0 + 4 hh + c with the constant
+        // c = 32 kb + 8 (r >> 2) + (r & 3); the limits are taken relative to
+        // k0 + 4 hh, so each score costs one compare with a constant per
+        // limit.
+        const int base = k0 + 4 * hh;
+        const int hi_rel = (BAND ? min(Nk - 1, qrow + off + win_right) : Nk - 1) - base;
+        const int lo_rel = BAND ? qrow + off - win_left - base : -(1 << 30);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int kr = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const int key = k0 + kr;
-            if (key > lim || key < lim_lo || ((badm >> (kr / WROWS)) & 1)) s[kb][r] = -INFINITY;
+            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+            const bool bad = MODE == kFwdPaged && ((badm >> ((c + 4 * hh) / WROWS)) & 1);
+            if (c > hi_rel || c < lo_rel || bad) s[kb][r] = -INFINITY;
           }
       }
 
