@@ -542,13 +542,19 @@ void fwd_bf16_kernel(
         const float mx2 = halves_max(mx) * scale_log2;
         if (wave_any(mx2 > m_run + kSlack)) {
           const float m_new = fmaxf(m_run, mx2);
-          const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+          // A row without a key so far has o = 0 and l = 0: the rescale
+          // changes nothing, and at d = 64 a wave whose rows are all such
+          // (its first tile) skips it (at d = 128 the branch cost six
+          // registers for a smaller share of the work).
+          if (!(D == 64 && __all(m_run == -INFINITY))) {
+            const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+            l_run *= alpha;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
+          }
           m_run = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[nb][r] *= alpha;
         }
         exps(m_run == -INFINITY ? 0.f : m_run);
       }
