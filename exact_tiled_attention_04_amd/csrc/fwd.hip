@@ -222,7 +222,11 @@ void fwd_bf16_kernel(
     split_unit<BAND>(wg / BH, n_qtiles, BR, Nq, Nk, BC, win_left, win_right, chunk_tiles, lane,
                      qt, chunk);
   } else {
-    grid_tile<MODE == kFwdRagged || MODE == kFwdPaged>(wg, n_qtiles, B, H, Hkv, qt, bh);
+    // Pair-major for packed sequences, and for dense rows without a mask,
+    // whose query tiles all carry the same work (no heavy-to-light
+    // imbalance for the order to cause).
+    grid_tile<MODE == kFwdRagged || MODE == kFwdPaged || (MODE == kFwdDense && !BAND)>(
+        wg, n_qtiles, B, H, Hkv, qt, bh);
   }
   const int b = bh / H;       // batch, or sequence of a packed batch
   const int h = bh % H;
