@@ -113,9 +113,10 @@ __device__ __forceinline__ int page_div(int key, const FwdSeqArgs& sq) {
 // of the group next to each other: the heads that share K and V run on one
 // L2 at the same time, each pair's K/V is fetched by one XCD, and every XCD
 // gets the same share of every sequence.  Within an XCD the order is either
-// query-tile layers across its pairs (dense rows: the heaviest tiles of every
-// head first) or PAIR_MAJOR, all tiles of one pair before the next (packed
-// sequences of different lengths: a pair's tiles stream its K/V together).
+// query-tile layers across its pairs (dense rows with a mask: the heaviest
+// tiles of every head first) or PAIR_MAJOR, all tiles of one pair before the
+// next (packed sequences of different lengths, and dense rows without a
+// mask, whose tiles are all equal: a pair's tiles stream its K/V together).
 // Otherwise consecutive workgroups take consecutive (batch, head) indices.
 template <bool PAIR_MAJOR>
 __device__ __forceinline__ void grid_tile(int wg, int n_qtiles, int B, int H, int Hkv, int& qt,
