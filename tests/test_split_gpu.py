@@ -133,3 +133,16 @@ def test_planner_split_shapes(gpu, B, H, Hkv, Nq, Nk, d, left, right):
     o_ref, lse_ref = oracle.forward(to64(q), to64(k), to64(v), scale, False, _band(left, right))
     check_out(to64(o), o_ref, "bf16")
     check_lse(to64(lse), lse_ref, "bf16")
+
+
+def test_forced_chunks_many_rounds(gpu):
+    """128-key parts over 16 causal heads of 2048 keys: 2176 units, about
+    three times the workgroups the GPU holds at once, so later units run in
+    later rounds; every row against the oracle."""
+    B, H, N, d = 1, 16, 2048, 128
+    q, k, v = workloads.prefill(B, H, 4, N, N, d, dtype="bf16", seed=21)
+    o, lse = attn.attn_fwd_splitkv(q.to(gpu), k.to(gpu), v.to(gpu), 0.09, -1, 0, chunk_keys=128)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.forward(to64(q), to64(k), to64(v), 0.09, True)
+    check_out(to64(o), o_ref, "bf16")
+    check_lse(to64(lse), lse_ref, "bf16")
