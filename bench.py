@@ -98,8 +98,9 @@ def _traffic(kernel, sources, per_launch_algorithmic):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this "
-              "build (the multi-GPU design is described, not built).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the "
+              "library runs on one GPU; sharding across GPUs is not implemented).",
+              file=sys.stderr)
         return 2
 
     import torch

@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, inconsistent strides */
-  ATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (e.g. d=96) */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid request the library does not implement (e.g. d=96) */
   ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query */
   ATTN_ERR_HIP = 4          /* the HIP runtime rejected a launch */
 } attn_status_t;
