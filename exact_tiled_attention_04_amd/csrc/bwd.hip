@@ -226,11 +226,18 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       // Lane (key jw, hh) register r holds query row q0 + 32 qb + 8 (r/4) + 4 hh + r%4.
       // Band edges: scores outside the band become -inf (P = 0), in one
       // block of selects taken only by the edge tiles.
+      // With base = q0 + 32 qb + 4 hh + off, register r's row position (query
+      // row + off) is base + c for the constant c = 8 (r / 4) + r % 4: the
+      // limits are taken relative to base, so each score costs one compare
+      // with a constant per limit.
       if (need_mask) {
+        const int base = q0 + 32 * qb + 4 * hh + off;
+        const int lo_c = jw - win_right - base;  // below: the key is right of the band
+        const int hi_c = jw + win_left - base;   // above: the key is left of the band
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int pos = q0 + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3) + off;
-          if (jw > pos + win_right || jw < pos - win_left) s[r] = -INFINITY;
+          const int c = 8 * (r >> 2) + (r & 3);
+          if (c < lo_c || c > hi_c) s[r] = -INFINITY;
         }
       }
       // dS without the softmax scale, which is applied once to dK at the end.
@@ -467,12 +474,16 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       const int lim = BAND ? min(Nk - 1, qrow + off + win_right) : Nk - 1;
       const int lim_lo = BAND ? qrow + off - win_left : 0;
       if (need_mask) {
+        // Key k0 + 4 hh + c with the constant c = 32 kb + 8 (r / 4) + r % 4:
+        // one compare with a constant per limit.
+        const int hi_c = lim - (k0 + 4 * hh);
+        const int lo_c = lim_lo - (k0 + 4 * hh);
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key > lim || key < lim_lo) s[kb][r] = -INFINITY;
+            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+            if (c > hi_c || c < lo_c) s[kb][r] = -INFINITY;
           }
       }
       // dS without the softmax scale, which is applied once to dQ at the end.
