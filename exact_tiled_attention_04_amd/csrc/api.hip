@@ -256,7 +256,8 @@ SplitPlan plan_fwd_split(int B, int H, int Nq, int Nk, int d, int left, int righ
   sp.units = units;
   sp.chunk_tiles = ct;
   sp.n_chunks = n_chunks;
-  sp.ws = (size_t)B * H * n_qt * n_chunks * 128 * (size_t)(d + 2) * sizeof(float);
+  // Per partial row: o / l in bf16, then the max and the sum in fp32.
+  sp.ws = (size_t)B * H * n_qt * n_chunks * 128 * (size_t)(2 * d + 2 * sizeof(float));
   return sp;
 }
 

@@ -203,35 +203,6 @@ __device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[D / 32], flo
   }
 }
 
-// The same for an fp32 tile (unnormalised partials): 64 columns (256 bytes
-// of a row) per pass through `stage` (32 * 256 bytes).
-template <int D>
-__device__ __forceinline__ void store_tile_rows_f32(const f32x16 (&acc)[D / 32], char* stage,
-                                                    float* dst, size_t row_stride,
-                                                    int rows_valid, int lane) {
-  const int li = lane & 31, hh = lane >> 5;
-#pragma unroll
-  for (int hf = 0; hf < D / 64; ++hf) {
-#pragma unroll
-    for (int nb2 = 0; nb2 < 2; ++nb2)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int c = 8 * nb2 + 2 * r4 + hh;  // columns 64 hf + 4 c .. + 3
-        f32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = acc[2 * hf + nb2][4 * r4 + e];
-        *(f32x4*)(stage + li * 256 + ((c ^ (li & 15)) * 16)) = w;
-      }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 4 * i + lane / 16;
-      const int c = lane % 16;
-      const f32x4 v = *(const f32x4*)(stage + r * 256 + ((c ^ (r & 15)) * 16));
-      if (r < rows_valid) *(f32x4*)(dst + (size_t)r * row_stride + 64 * hf + 4 * c) = v;
-    }
-  }
-}
-
 // Wave-uniform "any lane true".
 __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 

@@ -595,20 +595,22 @@ void fwd_bf16_kernel(
 
   const float l_tot = halves_sum(l_run);
   if (SPLIT && parts > 1) {
-    // Unnormalised partial: o (as whole rows through the wave's slice of the
-    // idle K/V buffers), the base-2 reference max and the sum, merged by
-    // fwd_merge_kernel.
+    // Partial of this key range, merged by fwd_merge_kernel: o / l in bf16
+    // (whole rows through the wave's slice of the idle K/V buffers, as the
+    // final O below), then the base-2 reference max and the sum l in fp32.
+    // Normalised, the bf16 rows hold values no larger than V's; the merge
+    // weights them by l 2^(m - M), so their rounding adds at most one bf16
+    // step of the largest |V| to O.
     const size_t prow0 = (((size_t)bh * n_qtiles + qt) * n_chunks + chunk) * BR + wave * 32;
-    static_assert(NW * 32 * 256 <= 4 * TILE, "partial staging fits the K/V buffers");
-    store_tile_rows_f32<D>(o, wave < 2 ? smem0 + wave * 32 * 256 : smem1 + (wave - 2) * 32 * 256,
-                           part + prow0 * D, D, Nq - wave_row_lo, lane);
-    if (qrow < Nq) {
-      const size_t prow = prow0 + li;
-      if (hh == 0) {
-        float* pml = part + (size_t)BH * n_qtiles * n_chunks * BR * D + prow * 2;
-        pml[0] = m_run;
-        pml[1] = l_tot;
-      }
+    __bf16* po = (__bf16*)part;
+    static_assert(NW * 32 * ROW <= 4 * TILE, "partial staging fits the K/V buffers");
+    store_tile_rows<D>(o, l_tot > 0.f ? 1.f / l_tot : 0.f,
+                       wave < 2 ? smem0 + wave * 32 * ROW : smem1 + (wave - 2) * 32 * ROW,
+                       po + prow0 * D, D, Nq - wave_row_lo, lane);
+    if (qrow < Nq && hh == 0) {
+      float* pml = (float*)(po + (size_t)BH * n_qtiles * n_chunks * BR * D) + (prow0 + li) * 2;
+      pml[0] = m_run;
+      pml[1] = l_tot;
     }
     return;
   }
@@ -626,9 +628,9 @@ void fwd_bf16_kernel(
 
 // Merge of the key-split partials of each query row (the split-context
 // algebra of "Attention kernels", FlashDecoding paragraph): M = max_c m_c,
-// w_c = 2^(m_c - M), l = sum_c w_c l_c, O = sum_c w_c o_c / l,
+// w_c = 2^(m_c - M) l_c, l = sum_c w_c, O = sum_c w_c (o_c / l_c) / l,
 // LSE = (M + log2 l) ln 2.  A tile of one part was written by its unit and
-// is skipped.  D/4 threads per row, four columns each (16-byte loads); each
+// is skipped.  D/4 threads per row, four columns each (8-byte loads); each
 // thread takes two rows 256 / (D/4) apart, with up to eight parts' loads of
 // both in flight.
 template <int D>
@@ -655,7 +657,8 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
   int parts = t_lo <= t_hi ? (t_hi - t_lo + chunk_tiles) / chunk_tiles : 0;
   if (parts == 1) return;
   parts = min(parts, n_chunks);
-  const float* ml = part + (size_t)BH * n_qtiles * n_chunks * BR * D;
+  const __bf16* po = (const __bf16*)part;
+  const float* ml = (const float*)(po + (size_t)BH * n_qtiles * n_chunks * BR * D);
   const size_t tile0 = ((size_t)bh * n_qtiles + qt) * n_chunks * BR;
   float big_m[PR], ell[PR];
   f32x4 acc[PR];
@@ -677,7 +680,11 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
         const size_t prow = tile0 + (size_t)(ok ? c0 + j : 0) * BR + (ok ? row % BR : 0);
         mv[i][j] = ok ? ml[prow * 2] : -INFINITY;
         lv[i][j] = ok ? ml[prow * 2 + 1] : 0.f;
-        ov[i][j] = ok ? *(const f32x4*)(part + prow * D + n4) : f32x4{};
+        const u32x2 pv = ok ? *(const u32x2*)(po + prow * D + n4) : u32x2{};
+        ov[i][j] = f32x4{__builtin_bit_cast(float, pv[0] << 16),
+                         __builtin_bit_cast(float, pv[0] & 0xffff0000u),
+                         __builtin_bit_cast(float, pv[1] << 16),
+                         __builtin_bit_cast(float, pv[1] & 0xffff0000u)};
       }
 #pragma unroll
     for (int i = 0; i < PR; ++i) {
@@ -690,8 +697,8 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(
       ell[i] *= r;
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        const float w = fast_exp2(mv[i][j] - bm);
-        ell[i] += w * lv[i][j];
+        const float w = fast_exp2(mv[i][j] - bm) * lv[i][j];
+        ell[i] += w;
         acc[i] += w * ov[i][j];
       }
       big_m[i] = bm;

@@ -110,10 +110,11 @@ attn_status_t attn_fwd_local(const void* Q, const void* K, const void* V, void* 
  * Bytes of workspace attn_fwd_splitkv needs (0 when it will not split the
  * key range for these sizes, or when the arguments are invalid).  Window
  * sides and chunk_keys as for attn_fwd_splitkv.  The workspace holds, per
- * query row and key part, the unnormalised partial result: the accumulator o
- * (fp32, d values), its reference maximum and its sum ("Attention kernels",
- * FlashDecoding paragraph: partials of separate key ranges, combined exactly
- * by rescaling with their maxima and sums).  Host function; no device work.
+ * query row and key part, the partial result: o / l (bf16, d values), then
+ * its reference maximum and its sum l (fp32) ("Attention kernels",
+ * FlashDecoding paragraph: partials of separate key ranges, combined by
+ * rescaling with their maxima and sums), 2 d + 8 bytes per row.  Host
+ * function; no device work.
  */
 size_t attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int window_left,
                                        int window_right, int chunk_keys);
@@ -121,7 +122,7 @@ size_t attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int 
 /*
  * attn_fwd_local for grids too small to fill the GPU: each 128-row query tile
  * may cut its key range into chunks computed by separate workgroups, whose
- * unnormalised partials (o, max, sum) are merged by max-rescaling.  "Modern
+ * partials (o / l in bf16, max and sum in fp32) are merged by rescaling.  "Modern
  * attention kernels", "Work partitioning in FlashAttention-2" (a grid with
  * too few independent programs leaves hardware idle); "Attention kernels",
  * FlashDecoding paragraph (split the keys, merge the partials exactly).
@@ -132,7 +133,7 @@ size_t attn_fwd_splitkv_workspace_size(int B, int H, int Nq, int Nk, int d, int 
  *   workspace    device scratch of attn_fwd_splitkv_workspace_size(...) bytes
  *                (16-byte aligned; may be NULL when that size is 0).
  * The result equals attn_fwd_local's within rounding (the order of the
- * floating-point sums differs).  dtype must be BF16 when a split happens.
+ * floating-point sums differs, and each partial is rounded to bf16 once).  dtype must be BF16 when a split happens.
  * Errors as attn_fwd_local, plus ATTN_ERR_INVALID_ARG for a bad chunk_keys
  * and ATTN_ERR_WORKSPACE for a missing or short workspace.
  */

@@ -250,9 +250,10 @@ def _one_round_part(tiles, heads, slots, least):
 
 def test_fwd_splitkv_workspace_queries(lib):
     # Forced 256-key parts over 1000 causal keys of d = 128 (32-key tiles): the
-    # last query tile sees 1000 keys = 32 tiles = 4 parts of 8 tiles.
+    # last query tile sees 1000 keys = 32 tiles = 4 parts of 8 tiles.  A
+    # partial row is o / l in bf16 (2 d bytes) plus the max and the sum in fp32.
     assert attn.attn_fwd_splitkv_workspace_size(1, 2, 1000, 1000, 128, -1, 0, 256) == \
-        2 * 8 * 4 * 128 * 130 * 4
+        2 * 8 * 4 * 128 * (2 * 128 + 8)
     assert attn.attn_fwd_splitkv_workspace_size(1, 2, 1000, 1000, 128, -1, 0, 100) == 0
     assert attn.attn_fwd_splitkv_workspace_size(1, 32, 8192, 8192, 128, -1, 0, 0) == 0
     # Planner, 4 heads x 8192 causal at d = 128: query tile i sees 4 (i + 1)
@@ -262,12 +263,12 @@ def test_fwd_splitkv_workspace_queries(lib):
     ct = _one_round_part(tiles, 4, 3 * 256, 20)
     assert ct == 52
     assert attn.attn_fwd_splitkv_workspace_size(1, 4, 8192, 8192, 128, -1, 0, 0) == \
-        4 * 64 * -(-256 // ct) * 128 * 130 * 4
+        4 * 64 * -(-256 // ct) * 128 * (2 * 128 + 8)
     # d = 64 (64-key tiles, 4 resident workgroups per CU), 4 heads x 4096.
     tiles = [2 * (i + 1) for i in range(32)]
     ct = _one_round_part(tiles, 4, 4 * 256, 10)
     assert attn.attn_fwd_splitkv_workspace_size(1, 4, 4096, 4096, 64, -1, 0, 0) == \
-        4 * 32 * -(-64 // ct) * 128 * 66 * 4
+        4 * 32 * -(-64 // ct) * 128 * (2 * 64 + 8)
     # One 128-row query tile against 512 keys: parts of at least 640 keys
     # would not split it.
     assert attn.attn_fwd_splitkv_workspace_size(1, 1, 128, 512, 128, -1, 0, 0) == 0
