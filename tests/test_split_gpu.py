@@ -146,3 +146,31 @@ def test_forced_chunks_many_rounds(gpu):
     o_ref, lse_ref = oracle.forward(to64(q), to64(k), to64(v), 0.09, True)
     check_out(to64(o), o_ref, "bf16")
     check_lse(to64(lse), lse_ref, "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_partials_within_their_bound(gpu, d):
+    """Each key-split partial is o / l rounded to bf16 once.  Rounding is at
+    most 2^-9 relative, and a partial's values are weighted means of V rows, so
+    the split output differs from the exact result by at most one rounding of
+    P, one of the partial and one of O: 3 * 2^-9 * max|V|; from the unsplit
+    kernel (its own P and O roundings) by at most 5 * 2^-9 * max|V|.  V is
+    scaled by 64 (|V| up to ~2^8) and the parts are 64 keys long (up to 16
+    per query tile)."""
+    N = 1000
+    q, k, v = workloads.prefill(1, 2, 2, N, N, d, dtype="bf16", seed=70 + d)
+    v = (v.float() * 64).to(torch.bfloat16)  # exact: a power-of-two scale
+    scale = 1.0 / math.sqrt(d)
+    qg, kg, vg = q.to(gpu), k.to(gpu), v.to(gpu)
+    o_s, lse_s = attn.attn_fwd_splitkv(qg, kg, vg, scale, -1, 0, chunk_keys=64)
+    o_u, _ = attn.attn_fwd(qg, kg, vg, scale, True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.forward(to64(q), to64(k), to64(v), scale, True)
+    vmax = float(v.float().abs().max())
+    err_ref = float(np.abs(to64(o_s) - o_ref).max())
+    err_unsplit = float(np.abs(to64(o_s) - to64(o_u)).max())
+    print(f"max|V| {vmax:.1f}: split vs oracle {err_ref:.3g} (bound {3 * 2**-9 * vmax:.3g}), "
+          f"vs unsplit {err_unsplit:.3g} (bound {5 * 2**-9 * vmax:.3g})")
+    assert err_ref <= 3 * 2**-9 * vmax
+    assert err_unsplit <= 5 * 2**-9 * vmax
+    check_lse(to64(lse_s), lse_ref, "bf16")
